@@ -1,0 +1,186 @@
+/*
+ * pa_verify.h -- C ABI of the paged verify-attention library (MI355X, gfx950).
+ *
+ * The operation (one speculative-decoding verify step of attention):
+ * every sequence b brings q_b query tokens (q_b = k + 1 for k draft tokens,
+ * 6 at MTP-5, up to 8) that attend, causally among themselves, to the
+ * sequence's own KV context. The context lives in a paged pool of 16-token
+ * blocks reached through a per-sequence block table; KV is bf16, or FP8 e4m3
+ * with one fp32 scale per token and KV head. The query heads that share a KV
+ * head are packed together (rows = q_b x G, G = Hq / Hkv).
+ *
+ * Sources:
+ *  - ATOM #2843, "keep MTP-5 decode on FlyDSL pa_decode past the gluon
+ *    query-length limit": Motivation (query length 6 at MTP-5; rows = query
+ *    length x GQA group = 48; per-token FP8 KV scales), Change (the decode
+ *    call receives the lengths, the block table, the query length, the K/V
+ *    scales, the sliding window and the context bound; sinks and windows are
+ *    layer properties), and the review thread on run_pa_decode (feasibility
+ *    is checked before any plan or scratch exists; a plan's cached scratch
+ *    means the call itself allocates nothing; a refused call fails loudly).
+ *  - ATOM #3091, "High-interactivity monokernel decode for
+ *    DeepSeek-V4.1-Flash on MI355X": Summary (contexts up to 1 Mi tokens;
+ *    paged-pool stores masked by row liveness, so padded requests write
+ *    nothing) and "How to reproduce" (16-token blocks, full graph capture).
+ *  - ATOM #3038, "[MiniMax-M3.1] P/D from a PP4 prefill into a TP4 decode
+ *    (2/2: DSpark)": Results (verify of 7 drafts + 1 = 8 tokens) and the KV
+ *    export commit message (pages are head-major per page); its review on
+ *    page geometry (no defaulted page size: the block size is an explicit,
+ *    checked argument).
+ *
+ * Meaning of a call (the plain definition the library computes, up to fp32
+ * rounding): for sequence b with context length L (the cache holds L tokens,
+ * the q new ones included), query row i in [0, q) sits at position
+ * p = L - q + i and sees the keys j with lo <= j <= p, where
+ * lo = max(0, p - W + 1) for a window of W keys (W = 0: lo = 0). With scores
+ * s_j = sigma * <Q[row], dequant(K_j)>, an optional sink logit z of the row's
+ * head, M = max(max_j s_j, z) and Z = sum_j e^(s_j - M) + e^(z - M):
+ *     out[row] = sum_j e^(s_j - M) dequant(V_j) / Z.
+ * dequant is the identity for bf16 and code x scale[token][kv head] for FP8.
+ *
+ * Layouts (all row-major, no padding between rows):
+ *  q            [T][Hq][D] bf16, T = sum_b q_b, sequence-major: sequence b's
+ *               rows start at t_b = q_0 + ... + q_(b-1)
+ *  k_pool/v_pool [num_blocks][Hkv][16][D] bf16, or uint8 e4m3 codes (OCP
+ *               e4m3fn: bias 7, max 448, NaN = 0x7F/0xFF)
+ *  k_scales/v_scales [num_blocks][Hkv][16] fp32 (a trailing [1] is the same
+ *               memory)
+ *  block_table  [B][max_blocks_per_seq] int32; entry n of row b is the pool
+ *               block holding tokens 16n..16n+15 of sequence b
+ *  sinks        mode 1: [Hq] fp32, one logit per head for every sequence;
+ *               mode 2: [B][Hq] fp32, -inf meaning "no sink"
+ *  out          [T][Hq][D], bf16 (round to nearest even) or fp32
+ *
+ * Ownership: every tensor belongs to the caller, who keeps it alive and
+ * unmodified until the stream work of the call has finished. A plan owns its
+ * work list, its copy of the lengths and windows, and its scratch; one plan
+ * serves one stream at a time (the scratch is not shared between calls in
+ * flight). Block-table contents (ids < num_blocks for every entry a sequence
+ * uses) and pointer validity are the caller's contract and are not checked.
+ */
+#ifndef PA_VERIFY_H
+#define PA_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_plan_s pa_plan_t; /* opaque plan */
+
+typedef enum {
+  PA_OK = 0,
+  PA_E_INVALID = 1,     /* a null pointer, a negative size, q_b > L_b, ... */
+  PA_E_UNSUPPORTED = 2, /* a meaningful shape this library does not serve */
+  PA_E_HIP = 3,         /* a HIP runtime call or a kernel launch failed */
+  PA_E_NOMEM = 4        /* device or host memory could not be allocated */
+} pa_status;
+
+typedef enum { PA_BF16 = 0, PA_FP8_E4M3 = 1, PA_FP32 = 2 } pa_dtype;
+
+/* Limits (a shape beyond them is refused with PA_E_UNSUPPORTED). */
+#define PA_BLOCK_TOKENS 16      /* tokens per KV block */
+#define PA_MAX_QUERY_LEN 8      /* q_b <= 8: verify of 7 drafts + 1 */
+#define PA_MAX_ROWS 64          /* q_b x G <= 64 packed rows per KV head */
+#define PA_MAX_CONTEXT 1048576  /* L_b <= 1 Mi tokens */
+
+typedef struct {
+  int32_t num_seqs;           /* B >= 1 */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* must be 16 (explicit: never defaulted) */
+  int32_t num_blocks;         /* pool capacity, >= 1 */
+  int32_t max_blocks_per_seq; /* block-table row stride in entries, >= 1 */
+  pa_dtype q_dtype;           /* PA_BF16 */
+  pa_dtype kv_dtype;          /* PA_BF16 or PA_FP8_E4M3 */
+  pa_dtype out_dtype;         /* PA_BF16 or PA_FP32 */
+  float softmax_scale;        /* sigma, finite and > 0 (e.g. 1/sqrt(D)) */
+  int32_t partition_tokens;   /* keys per work item (split-K unit): a
+                                 multiple of 16, or 0 to let the plan choose */
+  int32_t sinks_mode;         /* 0 none, 1 sinks[Hq], 2 sinks[B][Hq] */
+} pa_shape;
+
+/*
+ * Validate a shape and the per-sequence lengths, cut every sequence's
+ * visible keys into work items, and allocate the plan's device work list and
+ * scratch on `device`.
+ *   context_lens  host [B]: L_b, KV tokens in the cache including the q_b new
+ *                 ones; q_b <= L_b <= PA_MAX_CONTEXT
+ *   query_lens    host [B]: q_b in 0..PA_MAX_QUERY_LEN; 0 marks a padded slot
+ *                 that reads nothing and writes nothing
+ *   window        host [B] or NULL: W_b >= 0 keys per row including its own;
+ *                 0 = no window
+ *   device        HIP device ordinal, or -1 for a host-only plan (validation
+ *                 and work list, no HIP call and no device memory; useful for
+ *                 inspection; pa_decode_verify refuses it)
+ *   out           receives the plan; on any error *out = NULL and nothing
+ *                 stays allocated
+ * Every check runs before the first HIP call or allocation, so a refused
+ * shape costs nothing and leaks nothing. The host arrays are copied; the
+ * caller may free them on return. Thread-safe (no shared state).
+ */
+pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens,
+                  const int32_t* query_lens, const int32_t* window, int device,
+                  pa_plan_t** out);
+
+/*
+ * Run one verify-attention call with a plan: the partition kernel, then (if
+ * any sequence was split) the log-sum-exp reduce kernel, both enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream) of the plan's device,
+ * which must be the current device. Asynchronous: it allocates nothing,
+ * never synchronises, and may be captured in a HIP graph. Pointers are device
+ * pointers in the layouts above; k_scales/v_scales must be non-NULL exactly
+ * for FP8 KV, sinks non-NULL exactly for sinks_mode != 0. Rows of sequences
+ * with q_b = 0 are not written. Returns PA_E_INVALID for a missing pointer or
+ * a host-only plan (nothing is launched then) and PA_E_HIP if a launch fails.
+ */
+pa_status pa_decode_verify(const pa_plan_t* plan, const void* q,
+                           const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const float* k_scales,
+                           const float* v_scales, const float* sinks, void* out,
+                           void* stream);
+
+/* Release a plan and its device memory. NULL-safe. The caller makes sure no
+ * call that uses the plan is still in flight. */
+void pa_free(pa_plan_t* plan);
+
+/* Text of the last non-OK status returned on the calling thread. */
+const char* pa_last_error(void);
+
+/*
+ * Figures of a plan, each pointer optional:
+ *   kv_bytes        algorithmic KV bytes one call reads: for every active
+ *                   sequence, Hkv x (visible keys) x (K + V bytes per token,
+ *                   plus 8 bytes of FP8 scales)
+ *   scratch_bytes   device bytes of the partial results the plan owns
+ *   work_items      number of partition work items (workgroups launched)
+ *   partition_tokens keys per work item actually used
+ */
+pa_status pa_plan_info(const pa_plan_t* plan, int64_t* kv_bytes,
+                       int64_t* scratch_bytes, int32_t* work_items,
+                       int32_t* partition_tokens);
+
+/*
+ * Copy the plan's work list to host memory as rows of 5 int32:
+ * (sequence, kv head, first key, end key, partial slot or -1 when the item is
+ * the only one of its (sequence, kv head) and writes the output directly).
+ * Writes min(capacity, work_items) rows; returns PA_E_INVALID if items is
+ * NULL while capacity > 0.
+ */
+pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity);
+
+/*
+ * Optional timing hook: when both are non-NULL (hipEvent_t handles on the
+ * plan's device), every later pa_decode_verify records `before` just ahead of
+ * the partition kernel and `after` right behind it, on the call's stream.
+ * Pass NULLs to stop. Recording is the only effect; results are unchanged.
+ */
+pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_VERIFY_H */

@@ -1,0 +1,387 @@
+// Host side of the C ABI: validation, the work plan, scratch, launches.
+//
+// The plan follows the prior art's split between a host-built work plan with
+// its own cached scratch and an allocation-free call (ATOM #2843, review
+// thread on run_pa_decode: feasibility is checked right after the call's
+// arguments are known and before any plan or scratch is built; the call then
+// uses its plan's scratch and allocates none). Refusals name the limit they
+// hit and never fall back to another path (same page, vLLM bridge section:
+// fail loudly rather than compute a wrong answer).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pa_verify.h"
+#include "pa_internal.h"
+
+using namespace pav;
+
+struct pa_plan_s {
+  int device = -1;
+  pa_shape shape{};
+  std::vector<SeqInfo> seqs;
+  std::vector<WorkItem> items;
+  std::vector<ReduceItem> red;
+  int64_t kv_bytes = 0;
+  int64_t scratch_bytes = 0;
+  int32_t partition_tokens = 0;
+  int32_t rows_stride = 0;
+  int64_t n_slots = 0;
+  SeqInfo* d_seqs = nullptr;
+  WorkItem* d_items = nullptr;
+  ReduceItem* d_red = nullptr;
+  float* d_part_o = nullptr;
+  float* d_part_ml = nullptr;
+  hipEvent_t ev_before = nullptr;
+  hipEvent_t ev_after = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? PA_E_NOMEM : PA_E_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+void release_device(pa_plan_s* p) {
+  if (p->device < 0) return;
+  int cur = 0;
+  bool have = hipGetDevice(&cur) == hipSuccess;
+  if (have && cur != p->device) (void)hipSetDevice(p->device);
+  if (p->d_seqs) (void)hipFree(p->d_seqs);
+  if (p->d_items) (void)hipFree(p->d_items);
+  if (p->d_red) (void)hipFree(p->d_red);
+  if (p->d_part_o) (void)hipFree(p->d_part_o);
+  if (p->d_part_ml) (void)hipFree(p->d_part_ml);
+  p->d_seqs = nullptr;
+  p->d_items = nullptr;
+  p->d_red = nullptr;
+  p->d_part_o = nullptr;
+  p->d_part_ml = nullptr;
+  if (have && cur != p->device) (void)hipSetDevice(cur);
+}
+
+// Every check a call can fail, before anything is allocated.
+pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, const int32_t* win,
+                   int device) {
+  if (!s) return fail(PA_E_INVALID, "shape is NULL");
+  if (!ctx || !ql) return fail(PA_E_INVALID, "context_lens and query_lens are required");
+  if (device < -1) return fail(PA_E_INVALID, "device %d is not a device ordinal or -1", device);
+  if (s->num_seqs < 1) return fail(PA_E_INVALID, "num_seqs %d < 1", s->num_seqs);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(PA_E_INVALID, "head counts must be >= 1 (Hq %d, Hkv %d)", s->num_q_heads,
+                s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(PA_E_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->block_size != kBlock)
+    return fail(PA_E_UNSUPPORTED, "block_size %d: only 16-token blocks are served", s->block_size);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(PA_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are served", s->head_dim);
+  if (s->q_dtype != PA_BF16) return fail(PA_E_UNSUPPORTED, "q_dtype must be bf16");
+  if (s->kv_dtype != PA_BF16 && s->kv_dtype != PA_FP8_E4M3)
+    return fail(PA_E_UNSUPPORTED, "kv_dtype must be bf16 or fp8 e4m3");
+  if (s->out_dtype != PA_BF16 && s->out_dtype != PA_FP32)
+    return fail(PA_E_UNSUPPORTED, "out_dtype must be bf16 or fp32");
+  if (!(std::isfinite(s->softmax_scale) && s->softmax_scale > 0.f))
+    return fail(PA_E_INVALID, "softmax_scale must be finite and > 0");
+  if (s->num_blocks < 1) return fail(PA_E_INVALID, "num_blocks %d < 1", s->num_blocks);
+  if (s->max_blocks_per_seq < 1)
+    return fail(PA_E_INVALID, "max_blocks_per_seq %d < 1", s->max_blocks_per_seq);
+  if (s->partition_tokens < 0 || s->partition_tokens % kBlock != 0)
+    return fail(PA_E_INVALID, "partition_tokens %d must be 0 or a positive multiple of 16",
+                s->partition_tokens);
+  if (s->sinks_mode < 0 || s->sinks_mode > 2)
+    return fail(PA_E_INVALID, "sinks_mode %d is not 0, 1 or 2", s->sinks_mode);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  int64_t total_q = 0;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int L = ctx[b], q = ql[b];
+    if (q < 0) return fail(PA_E_INVALID, "query_lens[%d] = %d < 0", b, q);
+    if (q > kMaxQuery)
+      return fail(PA_E_UNSUPPORTED, "query_lens[%d] = %d exceeds the verify limit of %d", b, q,
+                  kMaxQuery);
+    if (L < q)
+      return fail(PA_E_INVALID, "context_lens[%d] = %d is smaller than its query length %d", b,
+                  L, q);
+    if (L > kMaxContext)
+      return fail(PA_E_UNSUPPORTED, "context_lens[%d] = %d exceeds the 1 Mi-token limit", b, L);
+    if ((L + kBlock - 1) / kBlock > s->max_blocks_per_seq)
+      return fail(PA_E_INVALID, "context_lens[%d] = %d needs %d blocks > max_blocks_per_seq %d",
+                  b, L, (L + kBlock - 1) / kBlock, s->max_blocks_per_seq);
+    if ((int64_t)(L + kBlock - 1) / kBlock > s->num_blocks)
+      return fail(PA_E_INVALID, "context_lens[%d] = %d needs more blocks than the pool holds", b,
+                  L);
+    if (win && win[b] < 0) return fail(PA_E_INVALID, "window[%d] = %d < 0", b, win[b]);
+    if (q * G > kMaxRows)
+      return fail(PA_E_UNSUPPORTED,
+                  "sequence %d packs %d x %d = %d rows per KV head; at most %d are served", b, q,
+                  G, q * G, kMaxRows);
+    total_q += q;
+  }
+  if (total_q * s->num_q_heads * (int64_t)s->head_dim > ((int64_t)1 << 40))
+    return fail(PA_E_UNSUPPORTED, "query tensor too large");
+  return PA_OK;
+}
+
+// Keys per work item when the caller leaves the choice to the plan: enough
+// items for about two rounds of one workgroup per CU, each large enough to
+// amortise its prologue and epilogue.
+int32_t auto_partition(int64_t total_keys) {
+  const int64_t target_items = 2 * 256;
+  int64_t p = (total_keys + target_items - 1) / target_items;
+  p = ((p + kChunk - 1) / kChunk) * kChunk;
+  p = std::max<int64_t>(p, 256);
+  p = std::min<int64_t>(p, 1 << 16);
+  return (int32_t)p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* query_lens,
+                  const int32_t* window, int device, pa_plan_t** out) {
+  if (!out) return fail(PA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  pa_status st = validate(shape, context_lens, query_lens, window, device);
+  if (st != PA_OK) return st;
+
+  const pa_shape& s = *shape;
+  const int B = s.num_seqs, Hkv = s.num_kv_heads, G = s.num_q_heads / s.num_kv_heads;
+  const int esz = s.kv_dtype == PA_FP8_E4M3 ? 1 : 2;
+  const int64_t tok_bytes = 2LL * s.head_dim * esz + (s.kv_dtype == PA_FP8_E4M3 ? 8 : 0);
+
+  pa_plan_s* p = new (std::nothrow) pa_plan_s();
+  if (!p) return fail(PA_E_NOMEM, "host allocation of the plan failed");
+  p->shape = s;
+  p->device = device;
+
+  try {
+    p->seqs.resize(B);
+    int64_t total_keys = 0;
+    int32_t q_off = 0, rows_stride = 0;
+    for (int b = 0; b < B; ++b) {
+      SeqInfo& si = p->seqs[b];
+      si.ctx_len = context_lens[b];
+      si.q_len = query_lens[b];
+      si.q_off = q_off;
+      si.window = window ? window[b] : 0;
+      si.lo = 0;
+      if (si.q_len > 0 && si.window > 0)
+        si.lo = std::max(0, si.ctx_len - si.q_len - si.window + 1);
+      si.n_parts = 0;
+      si.slot_base = -1;
+      q_off += si.q_len;
+      if (si.q_len > 0) {
+        total_keys += (int64_t)Hkv * (si.ctx_len - si.lo);
+        rows_stride = std::max(rows_stride, si.q_len * G);
+      }
+    }
+    p->rows_stride = rows_stride;
+    p->kv_bytes = total_keys * tok_bytes;
+    const int32_t P = s.partition_tokens > 0 ? s.partition_tokens : auto_partition(total_keys);
+    p->partition_tokens = P;
+
+    // Cut [lo, L) of every active sequence at multiples of P counted from
+    // lo rounded down to a page, the same cut for every KV head.
+    int64_t slots = 0;
+    for (int b = 0; b < B; ++b) {
+      SeqInfo& si = p->seqs[b];
+      if (si.q_len == 0) continue;
+      const int a = (si.lo / kBlock) * kBlock;
+      const int span = si.ctx_len - a;
+      si.n_parts = (span + P - 1) / P;
+      if (si.n_parts > 1) {
+        si.slot_base = (int32_t)slots;
+        slots += (int64_t)Hkv * si.n_parts;
+      }
+      for (int g = 0; g < Hkv; ++g) {
+        for (int k = 0; k < si.n_parts; ++k) {
+          WorkItem it{};
+          it.seq = b;
+          it.kv_head = g;
+          it.key_begin = std::max(si.lo, a + k * P);
+          it.key_end = std::min(si.ctx_len, a + (k + 1) * P);
+          it.slot = si.n_parts > 1 ? (int32_t)(si.slot_base + (int64_t)g * si.n_parts + k) : -1;
+          p->items.push_back(it);
+        }
+        if (si.n_parts > 1) {
+          ReduceItem r{b, g, (int32_t)(si.slot_base + (int64_t)g * si.n_parts), si.n_parts};
+          p->red.push_back(r);
+        }
+      }
+    }
+    if (p->items.size() >= (size_t)INT32_MAX || p->red.size() * 8 >= (size_t)INT32_MAX) {
+      delete p;
+      return fail(PA_E_UNSUPPORTED, "the work list exceeds a 1-D grid");
+    }
+    // Longest items first, so the short tails of split sequences fill in last.
+    std::stable_sort(p->items.begin(), p->items.end(), [](const WorkItem& x, const WorkItem& y) {
+      return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
+    });
+    p->n_slots = slots;
+    p->scratch_bytes = slots * rows_stride * ((int64_t)s.head_dim + 2) * 4;
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(PA_E_NOMEM, "host allocation of the work list failed");
+  }
+
+  if (device < 0) {
+    *out = p;
+    return PA_OK;
+  }
+
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipSetDevice");
+  }
+  auto upload = [&](void** dst, const void* src, size_t bytes) -> hipError_t {
+    if (bytes == 0) return hipSuccess;
+    hipError_t r = hipMalloc(dst, bytes);
+    if (r != hipSuccess) return r;
+    return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
+  };
+  e = upload((void**)&p->d_seqs, p->seqs.data(), p->seqs.size() * sizeof(SeqInfo));
+  if (e == hipSuccess)
+    e = upload((void**)&p->d_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  if (e == hipSuccess)
+    e = upload((void**)&p->d_red, p->red.data(), p->red.size() * sizeof(ReduceItem));
+  if (e == hipSuccess && p->n_slots > 0) {
+    e = hipMalloc((void**)&p->d_part_o,
+                  (size_t)p->n_slots * p->rows_stride * s.head_dim * sizeof(float));
+    if (e == hipSuccess)
+      e = hipMalloc((void**)&p->d_part_ml, (size_t)p->n_slots * p->rows_stride * 2 * sizeof(float));
+  }
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) {
+    release_device(p);
+    delete p;
+    return hip_fail(e, "allocating the plan's device memory");
+  }
+  *out = p;
+  return PA_OK;
+}
+
+pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table, const float* k_scales,
+                           const float* v_scales, const float* sinks, void* out, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+  const pa_shape& s = plan->shape;
+  const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
+  if (plan->items.empty()) return PA_OK;  // every sequence is a padded slot
+  if (!q || !k_pool || !v_pool || !block_table || !out)
+    return fail(PA_E_INVALID, "q, k_pool, v_pool, block_table and out are required");
+  if (fp8 && (!k_scales || !v_scales))
+    return fail(PA_E_INVALID, "FP8 KV needs k_scales and v_scales");
+  if (!fp8 && (k_scales || v_scales))
+    return fail(PA_E_INVALID, "bf16 KV takes no scales");
+  if (s.sinks_mode != 0 && !sinks) return fail(PA_E_INVALID, "sinks_mode %d needs sinks",
+                                               s.sinks_mode);
+  if (s.sinks_mode == 0 && sinks) return fail(PA_E_INVALID, "sinks given with sinks_mode 0");
+
+  KernelArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.sinks = sinks;
+  a.out = out;
+  a.part_o = plan->d_part_o;
+  a.part_ml = plan->d_part_ml;
+  a.items = plan->d_items;
+  a.seqs = plan->d_seqs;
+  a.red = plan->d_red;
+  a.num_q_heads = s.num_q_heads;
+  a.num_kv_heads = s.num_kv_heads;
+  a.group = s.num_q_heads / s.num_kv_heads;
+  a.max_blocks = s.max_blocks_per_seq;
+  a.rows_stride = plan->rows_stride;
+  a.sinks_mode = s.sinks_mode;
+  a.out_fp32 = s.out_dtype == PA_FP32;
+  a.scale_log2 = s.softmax_scale * kLog2e;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (plan->ev_before && (e = hipEventRecord(plan->ev_before, st)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, st);
+  if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  e = launch_reduce(a, (int)plan->red.size(), s.head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  return PA_OK;
+}
+
+void pa_free(pa_plan_t* plan) {
+  if (!plan) return;
+  release_device(plan);
+  delete plan;
+}
+
+pa_status pa_plan_info(const pa_plan_t* plan, int64_t* kv_bytes, int64_t* scratch_bytes,
+                       int32_t* work_items, int32_t* partition_tokens) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (kv_bytes) *kv_bytes = plan->kv_bytes;
+  if (scratch_bytes) *scratch_bytes = plan->scratch_bytes;
+  if (work_items) *work_items = (int32_t)plan->items.size();
+  if (partition_tokens) *partition_tokens = plan->partition_tokens;
+  return PA_OK;
+}
+
+pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (capacity > 0 && !items) return fail(PA_E_INVALID, "items is NULL");
+  const int32_t n = std::min<int32_t>(capacity, (int32_t)plan->items.size());
+  for (int32_t i = 0; i < n; ++i) {
+    const WorkItem& it = plan->items[i];
+    items[5 * i + 0] = it.seq;
+    items[5 * i + 1] = it.kv_head;
+    items[5 * i + 2] = it.key_begin;
+    items[5 * i + 3] = it.key_end;
+    items[5 * i + 4] = it.slot;
+  }
+  return PA_OK;
+}
+
+pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if ((before == nullptr) != (after == nullptr))
+    return fail(PA_E_INVALID, "give both events or neither");
+  plan->ev_before = static_cast<hipEvent_t>(before);
+  plan->ev_after = static_cast<hipEvent_t>(after);
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+"""The C ABI on the CPU: symbols, refusals before any allocation, the work list.
+
+No compute runs here. Validation happens before the first HIP call, so every
+refusal is testable without a GPU; host-only plans (device = -1) expose the
+work list the kernels would receive.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_verify_amd as pav
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "pa_verify.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\**\s+\**(pa_[a-z_]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "pa_plan" in names and "pa_decode_verify" in names and "pa_free" in names
+    lib = pav.library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pa_verify.h but not exported"
+    assert set(names) == set(pav.EXPORTED)
+
+
+def test_struct_layout_matches_header():
+    # 13 four-byte fields, no padding: the ctypes mirror must have the same size.
+    assert ctypes.sizeof(pav.PaShape) == 13 * 4
+
+
+def base_shape(**kw):
+    d = dict(num_seqs=2, num_q_heads=16, num_kv_heads=2, head_dim=128, num_blocks=4096,
+             max_blocks_per_seq=512, kv_dtype="bf16", out_dtype="bf16",
+             softmax_scale=0.088388, partition_tokens=0, sinks_mode=0)
+    d.update(kw)
+    return pav.make_shape(**d)
+
+
+REFUSALS = [
+    # (shape overrides, ctx, q, window, expected status, message fragment)
+    (dict(block_size=32), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "block_size"),
+    (dict(head_dim=96), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "head_dim"),
+    (dict(num_q_heads=15), [100, 50], [6, 6], None, pav.PA_E_INVALID, "multiple"),
+    (dict(num_seqs=0), [], [], None, pav.PA_E_INVALID, "num_seqs"),
+    (dict(kv_dtype="fp32"), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "kv_dtype"),
+    (dict(out_dtype="fp8"), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "out_dtype"),
+    (dict(q_dtype="fp32"), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "q_dtype"),
+    (dict(softmax_scale=0.0), [100, 50], [6, 6], None, pav.PA_E_INVALID, "softmax_scale"),
+    (dict(softmax_scale=float("nan")), [100, 50], [6, 6], None, pav.PA_E_INVALID, "softmax"),
+    (dict(partition_tokens=100), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
+    (dict(partition_tokens=-16), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
+    (dict(sinks_mode=3), [100, 50], [6, 6], None, pav.PA_E_INVALID, "sinks_mode"),
+    ({}, [100, 50], [9, 6], None, pav.PA_E_UNSUPPORTED, "verify limit"),
+    ({}, [100, 50], [-1, 6], None, pav.PA_E_INVALID, "< 0"),
+    ({}, [5, 50], [6, 6], None, pav.PA_E_INVALID, "smaller than its query"),
+    ({}, [(1 << 20) + 1, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "1 Mi"),
+    (dict(max_blocks_per_seq=4), [100, 50], [6, 6], None, pav.PA_E_INVALID, "max_blocks"),
+    (dict(num_blocks=3), [100, 50], [6, 6], None, pav.PA_E_INVALID, "pool"),
+    ({}, [100, 50], [6, 6], [-1, 0], pav.PA_E_INVALID, "window"),
+    (dict(num_q_heads=32, num_kv_heads=2), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED,
+     "rows"),
+    (dict(num_q_heads=16, num_kv_heads=1), [100, 50], [5, 1], None, pav.PA_E_UNSUPPORTED,
+     "rows"),
+]
+
+
+@pytest.mark.parametrize("device", [-1, 0])
+@pytest.mark.parametrize("case", REFUSALS, ids=[c[5] + str(i) for i, c in enumerate(REFUSALS)])
+def test_refusals_happen_before_anything_is_built(case, device):
+    """Each refusal is returned by validation alone (also with device 0 on a
+    box without a GPU: no HIP call is reached), names its limit, and leaves
+    *out NULL."""
+    over, ctx, q, win, status, frag = case
+    shape = base_shape(**over) if "num_seqs" in over else base_shape(num_seqs=len(ctx), **over)
+    out = ctypes.c_void_p(1234)
+    arr = lambda v: None if v is None else (ctypes.c_int32 * max(len(v), 1))(*v)
+    st = pav.library().pa_plan(ctypes.byref(shape), arr(ctx), arr(q), arr(win), device,
+                               ctypes.byref(out))
+    assert st == status, pav.pa_last_error()
+    assert out.value is None
+    assert frag.lower() in pav.pa_last_error().lower()
+
+
+def test_null_arguments_are_refused():
+    shape = base_shape()
+    out = ctypes.c_void_p()
+    ctx = (ctypes.c_int32 * 2)(100, 50)
+    q = (ctypes.c_int32 * 2)(6, 6)
+    lib = pav.library()
+    assert lib.pa_plan(None, ctx, q, None, -1, ctypes.byref(out)) == pav.PA_E_INVALID
+    assert lib.pa_plan(ctypes.byref(shape), None, q, None, -1, ctypes.byref(out)) == pav.PA_E_INVALID
+    assert lib.pa_plan(ctypes.byref(shape), ctx, q, None, -1, None) == pav.PA_E_INVALID
+    assert lib.pa_decode_verify(None, None, None, None, None, None, None, None, None,
+                                None) == pav.PA_E_INVALID
+    lib.pa_free(None)  # NULL-safe
+
+
+def test_host_only_plan_refuses_to_run():
+    plan = pav.pa_plan(base_shape(), [100, 50], [6, 6], None, device=-1)
+    with pytest.raises(pav.PaError) as e:
+        pav.library()
+        st = pav.library().pa_decode_verify(plan.handle, 1, 1, 1, 1, None, None, None, 1, None)
+        pav._check(st)
+    assert e.value.status == pav.PA_E_INVALID
+    plan.close()
+
+
+def check_worklist(plan, ctx, q, win, Hkv, P=None):
+    """Items of every (sequence, kv head) tile its visible keys exactly once,
+    in page-aligned pieces; slots are unique; single items write directly."""
+    items = plan.items()
+    info = plan.info()
+    assert info["work_items"] == len(items)
+    P = P or info["partition_tokens"]
+    per = {}
+    slots = set()
+    for (b, g, k0, k1, slot) in items:
+        assert 0 <= g < Hkv and k0 < k1 and (k1 - k0) <= P
+        per.setdefault((b, g), []).append((k0, k1, slot))
+        if slot >= 0:
+            assert slot not in slots
+            slots.add(slot)
+    for b, (L, qb) in enumerate(zip(ctx, q)):
+        W = win[b] if win else 0
+        for g in range(Hkv):
+            if qb == 0:
+                assert (b, g) not in per
+                continue
+            lo = max(0, L - qb - W + 1) if W > 0 else 0
+            segs = sorted(per[(b, g)])
+            assert segs[0][0] == lo and segs[-1][1] == L
+            for (a0, a1, _), (b0, _, _) in zip(segs, segs[1:]):
+                assert a1 == b0 and a1 % 16 == 0
+            if len(segs) == 1:
+                assert segs[0][2] == -1
+            else:
+                assert all(s >= 0 for _, _, s in segs)
+    return items
+
+
+@pytest.mark.parametrize("P", [0, 16, 64, 512, 4096])
+def test_worklist_tiles_visible_keys(P):
+    ctx = [37, 100, 4096, 17, 8, 20000, 1]
+    q = [1, 3, 6, 8, 0, 5, 1]
+    win = [0, 40, 0, 0, 0, 4096, 0]
+    shape = base_shape(num_seqs=len(ctx), partition_tokens=P, max_blocks_per_seq=2048)
+    plan = pav.pa_plan(shape, ctx, q, win, device=-1)
+    check_worklist(plan, ctx, q, win, 2, P or None)
+    plan.close()
+
+
+def test_worklist_for_named_workloads():
+    for cfg in (1, 2, 3, 5):
+        wl = workloads.make(cfg, scale_ctx=0.25) if cfg != 1 else workloads.make(1)
+        plan = pav.plan_for(wl, device=-1)
+        win = None if wl.window is None else wl.window.tolist()
+        check_worklist(plan, wl.ctx_lens.tolist(), wl.q_lens.tolist(), win, wl.num_kv_heads)
+        assert plan.info()["kv_bytes"] == wl.kv_bytes()
+        plan.close()
+
+
+def test_long_context_partitions():
+    wl_shape = base_shape(num_seqs=1, max_blocks_per_seq=65536, num_blocks=131072,
+                          partition_tokens=512)
+    plan = pav.pa_plan(wl_shape, [1 << 20], [6], None, device=-1)
+    info = plan.info()
+    assert info["work_items"] == 2 * (1 << 20) // 512
+    assert info["kv_bytes"] == 2 * (1 << 20) * 512
+    # partials: one (rows x (D + 2)) fp32 record per item
+    assert info["scratch_bytes"] == info["work_items"] * 48 * (128 + 2) * 4
+    plan.close()
+
+
+def test_all_padded_slots_plan_nothing():
+    plan = pav.pa_plan(base_shape(num_seqs=3), [10, 20, 30], [0, 0, 0], None, device=-1)
+    assert plan.info()["work_items"] == 0 and plan.info()["kv_bytes"] == 0
+    plan.close()
