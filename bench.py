@@ -1,0 +1,318 @@
+"""Bench: paged verify attention on one MI355X.
+
+Prints ONE JSON line. The headline workload is MTP-5 verify with bf16 KV
+(8 sequences, query length 6, 16 q / 2 KV heads, D 128, contexts uniform in
+[4096, 32768], 16-token pages); a step is one pa_decode_verify call (the
+partition kernel and the log-sum-exp reduce) over that batch with its inputs
+already in HBM. The metric is the algorithmic KV bytes a call must read
+(K + V, plus FP8 scales) divided by the time per call.
+
+Cache hygiene: the MI355X's 256 MiB Infinity Cache would hold a ~150 MB
+working set, so consecutive steps rotate over enough copies of the K/V pools
+that every call's KV was last touched more than 1 GiB of traffic earlier.
+No flush runs inside the timed region.
+
+Timing: the K timed steps are one replay of a HIP graph that captured them
+(as a serving engine replays decode steps); the host clock around it, with
+device synchronisations on both sides, gives ms_per_step.
+
+Roofline: the partition kernel dominates; its duration is read from HIP
+events recorded around it on the call's stream (pa_set_partition_events)
+in an eager pass over the same calls.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV-read HBM GB/s (% of peak) + µs/call, q=6 verify, bf16 & FP8 KV"
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_verify_amd", "csrc", "pa_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload_key: str):
+    """HBM bytes per partition launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measure(wl, steps: int, warmup: int, partition_tokens=None):
+    """Time `steps` calls on rotating pool copies; returns a dict of figures.
+
+    The timed region is one replay of a HIP graph holding the `steps` calls
+    (the way a serving engine replays its decode steps), bracketed by device
+    synchronisations and the host clock; if capture is unavailable the same
+    steps run eagerly. A second, eager pass over the same calls records HIP
+    events around every partition kernel on its stream, which give that
+    kernel's duration per call.
+    """
+    import torch
+
+    import paged_kv_cache_verify_amd as pav
+
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0, partition_tokens=partition_tokens)
+    info = plan.info()
+    kv = info["kv_bytes"]
+    copies = 1 if kv >= (1 << 30) else int(math.ceil((1 << 30) / kv)) + 1
+    pools = [(dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales)]
+    for _ in range(copies - 1):
+        pools.append(tuple(None if t is None else t.clone() for t in pools[0]))
+    dt = torch.float32 if wl.out_dtype == "fp32" else torch.bfloat16
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda:0")
+    s = torch.cuda.Stream()
+
+    def call(i):
+        kp, vp, ks, vs = pools[i % copies]
+        pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out, s)
+
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+
+    mode = "hip-graph replay"
+    g = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                call(warmup + i)
+        with torch.cuda.stream(s):
+            g.replay()  # untimed: first replay
+        torch.cuda.synchronize()
+    except Exception as exc:  # pragma: no cover - depends on the runtime
+        log(f"  graph capture unavailable ({exc}); timing eager calls")
+        g = None
+        mode = "eager launches"
+        torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        t_start.record(s)
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(steps):
+                call(warmup + i)
+        t_end.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    # The same calls launched one by one, with HIP events recorded around
+    # every partition kernel on its stream (events inside a replayed graph
+    # do not time the node they surround).
+    with torch.cuda.stream(s):
+        for e in ev_b + ev_a:
+            e.record(s)  # creates the HIP events
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for i in range(steps):
+            pav.pa_set_partition_events(plan, ev_b[i], ev_a[i])
+            call(i)
+    torch.cuda.synchronize()
+    eager = time.perf_counter() - e0
+    pav.pa_set_partition_events(plan, None, None)
+    part_ms = [b.elapsed_time(a) for b, a in zip(ev_b, ev_a)]
+    del g
+    pav.pa_free(plan)
+    return {
+        "kv_bytes": kv,
+        "copies": copies,
+        "plan": info,
+        "mode": mode,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "event_ms_per_step": t_start.elapsed_time(t_end) / steps,
+        "eager_ms_per_step": 1e3 * eager / steps,
+        "partition_ms_mean": statistics.fmean(part_ms),
+        "partition_ms_median": statistics.median(part_ms),
+        "partition_ms_p90": sorted(part_ms)[int(0.9 * (len(part_ms) - 1))],
+    }
+
+
+def cpu_baseline(wl, budget_s: float = 10.0):
+    """The oracle as it stands, on the host cores, over the same workload."""
+    import oracle
+
+    threads = oracle.default_threads()
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.verify(wl, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if (time.perf_counter() - t_all > budget_s and len(times) >= 3) or len(times) >= 40:
+            break
+    per_call = statistics.median(times)
+    return {
+        "value": round(wl.kv_bytes() / per_call / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"the whole workload (all {wl.num_seqs} sequences), fp64 oracle, median of "
+                   f"{len(times)} runs: {per_call:.2f} s per call; host "
+                   f"{platform.processor() or platform.machine()}, os.cpu_count()="
+                   f"{os.cpu_count()}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the FP8, long-context and mixed workloads")
+    ap.add_argument("--only", type=int, default=None,
+                    help="time just this workload (2..5) and print its figures")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by KV head, sequence or context; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+        del src, dst
+
+    main_cfg = args.only or 2
+    log(f"generating workload {main_cfg} ...")
+    wl = workloads.make(main_cfg)
+    log(f"  {wl.name}: L={wl.ctx_lens.tolist()} kv_bytes={wl.kv_bytes()}")
+    r = measure(wl, args.steps, args.warmup, args.partition_tokens)
+    ms = r["wall_ms_per_step"]
+    value = r["kv_bytes"] / (ms * 1e-3) / 1e9
+    achieved = r["kv_bytes"] / (r["partition_ms_mean"] * 1e-3) / 1e9
+    log(f"  wall {1e3 * ms:.1f} us/step ({value:.0f} GB/s, {r['mode']}), events "
+        f"{1e3 * r['event_ms_per_step']:.1f} us/step, partition kernel mean "
+        f"{1e3 * r['partition_ms_mean']:.1f} us (median {1e3 * r['partition_ms_median']:.1f}, "
+        f"p90 {1e3 * r['partition_ms_p90']:.1f}) = {achieved:.0f} GB/s, eager "
+        f"{1e3 * r['eager_ms_per_step']:.1f} us/step; plan {r['plan']}, {r['copies']} pool copies")
+
+    key = f"workload{main_cfg}"
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 Q",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}, seed {wl.seed}",
+            "kv_bytes_per_call": r["kv_bytes"],
+            "us_per_call": round(1e3 * ms, 2),
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "timed_as": r["mode"],
+            "us_per_call_eager_launches": round(1e3 * r["eager_ms_per_step"], 2),
+            "partition_tokens": r["plan"]["partition_tokens"],
+            "work_items": r["plan"]["work_items"],
+            "pool_copies_rotated": r["copies"],
+            "context_lens": wl.ctx_lens.tolist(),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(key),
+            "partition_us_mean": round(1e3 * r["partition_ms_mean"], 2),
+        },
+    }
+
+    if not args.no_extra and args.only is None:
+        extra = {}
+        for cfg, P in ((3, None), (5, None), (4, 512), (4, 0)):
+            wlx = workloads.make(cfg)
+            log(f"workload {cfg}, partition {P or 'auto'}: {wlx.name}")
+            rx = measure(wlx, max(20, args.steps // 4), max(5, args.warmup // 4), P)
+            msx = rx["wall_ms_per_step"]
+            gbs = rx["kv_bytes"] / (msx * 1e-3) / 1e9
+            ach = rx["kv_bytes"] / (rx["partition_ms_mean"] * 1e-3) / 1e9
+            log(f"  {1e3 * msx:.1f} us/call = {gbs:.0f} GB/s ({rx['mode']}); partition kernel "
+                f"{1e3 * rx['partition_ms_mean']:.1f} us = {ach:.0f} GB/s; eager "
+                f"{1e3 * rx['eager_ms_per_step']:.1f} us/call; plan {rx['plan']}")
+            extra[f"workload {cfg}" + ("" if P is None else f" (partition {P or 'auto'})")] = {
+                "us_per_call": round(1e3 * msx, 2),
+                "us_per_call_eager_launches": round(1e3 * rx["eager_ms_per_step"], 2),
+                "GB_s": round(gbs, 1),
+                "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "partition_kernel_GB_s": round(ach, 1),
+                "kv_bytes_per_call": rx["kv_bytes"],
+                "work_items": rx["plan"]["work_items"],
+                "partition_tokens": rx["plan"]["partition_tokens"],
+            }
+            del wlx
+        line["other_workloads"] = extra
+
+    if not args.no_cpu_baseline and args.only is None:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+        log(f"  {line['cpu_baseline']}")
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -84,6 +84,7 @@ typedef enum { PA_BF16 = 0, PA_FP8_E4M3 = 1, PA_FP32 = 2 } pa_dtype;
 #define PA_MAX_QUERY_LEN 8      /* q_b <= 8: verify of 7 drafts + 1 */
 #define PA_MAX_ROWS 64          /* q_b x G <= 64 packed rows per KV head */
 #define PA_MAX_CONTEXT 1048576  /* L_b <= 1 Mi tokens */
+#define PA_MAX_ITEM_KEYS 8192   /* partition_tokens <= 8192 */
 
 typedef struct {
   int32_t num_seqs;           /* B >= 1 */
@@ -98,7 +99,8 @@ typedef struct {
   pa_dtype out_dtype;         /* PA_BF16 or PA_FP32 */
   float softmax_scale;        /* sigma, finite and > 0 (e.g. 1/sqrt(D)) */
   int32_t partition_tokens;   /* keys per work item (split-K unit): a
-                                 multiple of 16, or 0 to let the plan choose */
+                                 multiple of 16 up to PA_MAX_ITEM_KEYS, or 0
+                                 to let the plan choose */
   int32_t sinks_mode;         /* 0 none, 1 sinks[Hq], 2 sinks[B][Hq] */
 } pa_shape;
 

@@ -185,6 +185,9 @@ def pa_free(plan: Plan) -> None:
 def pa_set_partition_events(plan: Plan, before=None, after=None) -> None:
     """Record torch.cuda.Event handles around the partition kernel (or stop,
     with None)."""
+    for ev in (before, after):
+        if ev is not None and not ev.cuda_event:
+            ev.record()  # torch creates its HIP event on the first record
     b = ctypes.c_void_p(before.cuda_event) if before is not None else None
     a = ctypes.c_void_p(after.cuda_event) if after is not None else None
     plan._events = (before, after)

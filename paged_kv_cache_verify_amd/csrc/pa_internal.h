@@ -14,6 +14,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxRows = 64;    // q x G packed rows per KV head (4 MFMA row tiles)
 constexpr int kMaxQuery = 8;
 constexpr int kMaxContext = 1 << 20;
+// Keys per work item: each wave keeps the page ids of its (at most 64)
+// chunks in one register, one chunk per lane.
+constexpr int kMaxItemKeys = 64 * kWaves * kChunk;  // 8192
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One workgroup's share of the work: the keys [key_begin, key_end) of one
@@ -25,7 +28,12 @@ struct WorkItem {
   int32_t key_begin;
   int32_t key_end;
   int32_t slot;
-  int32_t pad[3];
+  // the sequence's fields, repeated here so one load brings everything
+  int32_t ctx_len;
+  int32_t q_len;
+  int32_t q_off;
+  int32_t window;
+  int32_t pad[7];
 };
 
 struct SeqInfo {

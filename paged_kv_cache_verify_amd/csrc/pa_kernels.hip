@@ -1,25 +1,24 @@
 // gfx950 kernels for paged verify attention.
 //
 // Partition kernel: one workgroup (4 waves) per work item = the keys
-// [key_begin, key_end) of one (sequence, KV head). Every wave takes every
-// 4th 32-token chunk (two 16-token pages) of the item and keeps its own
-// online-softmax state for all q x G packed rows of the KV head; the four
-// states are merged in LDS at the end. Per chunk a wave
-//   1. reads the two page ids from the block table (wave-uniform),
-//   2. loads K straight from HBM into MFMA A-operand registers (token on M,
-//      16 contiguous bytes per lane) and V in token-major 1 KiB slabs,
-//      both one chunk ahead of use,
-//   3. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (FP8 codes are
-//      first converted exactly to bf16 in registers; the per-token K scale
-//      multiplies the scores),
-//   4. masks (causal within the query, window, key range) by selecting -inf,
-//   5. runs the online softmax in the exp2 domain (row max over 16-lane
-//      groups via cross-lane exchange),
-//   6. writes V transposed-on-read into a wave-private, XOR-swizzled LDS
-//      tile (invalid tokens zeroed), gathers the V^T A-operand, and
-//      accumulates O^T += V^T P^T, the P^T B-operand coming straight from the
-//      S^T accumulator registers (the per-token V scale folded into P).
-// The log-sum-exp reduce kernel merges the partial (O, m, l) of split pairs.
+// [key_begin, key_end) of one (sequence, KV head), all q x G packed rows of
+// that KV head. The item's keys stream through an LDS ring of R stages, one
+// 32-token chunk (two 16-token pages) per stage, filled by direct
+// global-to-LDS loads that the four waves issue together (K in MFMA
+// A-operand order, V into an XOR-swizzled token-major tile); one barrier per
+// chunk recycles a stage. Each wave owns one tile of 16 rows and, per chunk,
+//   1. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, tokens on the M
+//      index (FP8 codes are converted exactly to bf16 first and the per-token
+//      K scale multiplies the scores),
+//   2. masks (causal within the query, window, key range) by selecting -inf,
+//   3. runs an online softmax in the exp2 domain whose reference max only
+//      moves when a chunk beats it by 2^8 (rare rescaling),
+//   4. accumulates O^T += V^T P^T: V^T comes from ds_read_b64_tr_b16 (or
+//      _tr_b8 for FP8) on the tile, P^T straight from the S^T accumulator
+//      registers as a bf16 hi+lo pair (the per-token V scale folded in).
+// A wave's state never leaves its registers, so the epilogue writes the
+// output (or this item's partial) directly. The log-sum-exp reduce kernel
+// merges the partials of split (sequence, KV head) pairs.
 //
 // Sources: ATOM #2843 ("keep MTP-5 decode on FlyDSL pa_decode past the gluon
 // query-length limit", Motivation and Follow-up in aiter: rows = query length
@@ -78,16 +77,34 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the MFMA's four lane
+// groups holding one row). v_permlane16_swap / v_permlane32_swap exchange
+// rows of two registers; applied to two copies of v they leave the pair
+// (v[l], v[l^16]) resp. (v[l], v[l^32]) in the two registers. Issued from asm
+// on two distinct copies: the compiler folds the builtin's two results into
+// one when both inputs are the same value. s_nop 1 covers the VALU-write to
+// permlane-read hazard.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ float xlane_max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a = v, b = v;
+  swap16(a, b);
+  float c = fmaxf(a, b), d = c;
+  swap32(c, d);
+  return fmaxf(c, d);
 }
 
 __device__ __forceinline__ float xlane_sum4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a = v, b = v;
+  swap16(a, b);
+  float c = a + b, d = c;
+  swap32(c, d);
+  return c + d;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -129,441 +146,544 @@ __device__ __forceinline__ i32x2 lds_tr8(const unsigned char* base, int off) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PAV_LDS i32x2*)(base + off));
 }
 
+
+// ---------------------------------------------------------------------------
+// The LDS ring.
+// ---------------------------------------------------------------------------
+
+constexpr int kRingBytes = 48 * 1024;  // per workgroup: three workgroups fit in a CU
+constexpr int kMaxChunks = kMaxItemKeys / kChunk + 1;
+
 template <int D, bool FP8>
-struct ChunkRegs {
-  u32x4 k[2][Cfg<D, FP8>::KLD];
-  u32x4 v[Cfg<D, FP8>::VLD];
-  f32x4 ks[2];
-  f32x4 vs[2];
+struct Ring {
+  using C = Cfg<D, FP8>;
+  static constexpr int KB = 2 * C::KLD * 1024;   // K of two pages, operand order
+  static constexpr int VB = C::VLD * 1024;       // V tile of two pages
+  static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
+  static constexpr int STAGE = KB + VB + SB;
+  static constexpr int R = kRingBytes / STAGE;   // stages
+  static constexpr int T = 2 * C::KLD + C::VLD;  // 1 KiB loads per chunk
+  static constexpr int TW = T / kWaves;          // ... issued by each wave
+  static_assert(T % kWaves == 0, "every wave issues the same number of loads");
+  static_assert(R >= 3, "the ring needs at least three stages");
+  // Loads a wave may still have in flight when it starts on a chunk: those
+  // of the next R - 2 chunks (wave 0 also loads the FP8 scales).
+  static constexpr int WAIT = (R - 2) * TW;
+  static constexpr int WAIT0 = (R - 2) * (TW + (FP8 ? 1 : 0));
+  static_assert(WAIT0 <= 63, "vmcnt holds at most 63");
 };
 
-struct Smem {
-  // The V tiles (4 x 32 x D, at most 32 KiB) alias the merge buffers.
-  float buf[kWaves][kMaxRows][128];
-  float2 ml[kWaves][kMaxRows];
+struct __align__(16) Smem {
+  unsigned char ring[kRingBytes];
+  int32_t pages[2 * kMaxChunks];  // page ids of each chunk's two pages
 };
 
-struct PageIds {
-  int a, b;
-};
+#define PAV_LDS_VOID __attribute__((address_space(3))) void
 
-__device__ __forceinline__ PageIds page_ids(const int32_t* bt, int tok0, int tv1) {
-  const int pg = tok0 >> 4;
-  PageIds p;
-  p.a = bt[pg];
-  p.b = (tok0 + kBlock < tv1) ? bt[pg + 1] : p.a;  // never read past the last page
-  return p;
+// Direct global-to-LDS loads: every lane moves `size` bytes from its own
+// address to lds_dst + size * lane (lds_dst is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (PAV_LDS_VOID*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (PAV_LDS_VOID*)lds_dst, 4, 0, 0);
 }
 
+// Wait until at most N of this wave's vector-memory operations are pending.
+// The compiler does not order direct-to-LDS loads before the LDS reads of
+// their data, so the ring's waits are explicit; the memory clobber keeps
+// later LDS reads below the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the ring: this wave's LDS reads and writes are done
+// (lgkmcnt 0) before it arrives. Unlike __syncthreads() it does not drain
+// vector-memory operations, so the loads of later stages stay in flight;
+// each wave has already waited for its own loads of the stage it needs.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The wave's share of chunk k's loads into stage `sb`. Wave 0 / 1 load K
+// of the chunk's first / second page (KLD loads of 1 KiB, in MFMA operand
+// order: lane l of load u sits at byte 1024 u + 16 l and is what lane l of
+// the MFMA reads back); wave 2 / 3 load V of the first / second page into
+// the swizzled tile (lane l fetches whichever source chunk belongs at its
+// tile position). Wave 0 also loads the FP8 scales.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_k(ChunkRegs<D, FP8>& R, const KernelArgs& A, PageIds pid,
-                                       int g, int lane) {
+__device__ __forceinline__ void issue_chunk(const KernelArgs& A, const Smem& sm,
+                                            unsigned char* sb, int k, int g, int w, int lane) {
   using C = Cfg<D, FP8>;
+  using RG = Ring<D, FP8>;
+  static_assert(RG::TW == C::KLD && 2 * RG::TW == C::VLD, "one page of K or V per wave");
   const int n = lane & 15, c = lane >> 4;
-  const char* kp = static_cast<const char*>(A.k_pool);
-  const int64_t baseA = ((int64_t)pid.a * A.num_kv_heads + g) * C::BLKB;
-  const int64_t baseB = ((int64_t)pid.b * A.num_kv_heads + g) * C::BLKB;
+  const int half = w & 1;
+  const int page = __builtin_amdgcn_readfirstlane(sm.pages[2 * k + half]);
+  const int64_t base = ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
+  if (w < 2) {
+    const char* src = static_cast<const char*>(A.k_pool) + base + n * C::ROWB + 16 * c;
+    unsigned char* dst = sb + half * C::KLD * 1024;
 #pragma unroll
-  for (int u = 0; u < C::KLD; ++u) {
-    const int off = n * C::ROWB + 64 * u + 16 * c;
-    R.k[0][u] = *reinterpret_cast<const u32x4*>(kp + baseA + off);
-    R.k[1][u] = *reinterpret_cast<const u32x4*>(kp + baseB + off);
+    for (int u = 0; u < C::KLD; ++u) dma16(src + 64 * u, dst + u * 1024);
+  } else {
+    const char* src = static_cast<const char*>(A.v_pool) + base;
+    unsigned char* dst = sb + RG::KB + half * (C::BLKB);
+#pragma unroll
+    for (int u = 0; u < C::VLD / 2; ++u) {
+      const int pos = u * 1024 + lane * 16;  // byte position in this page's half of the tile
+      const int tp = pos / C::ROWB;          // token within the page
+      const int t = 16 * half + tp;          // token within the chunk (sets the swizzle)
+      const int ch = ((pos % C::ROWB) >> 4) ^ vswz<D, FP8>(t);  // its source chunk
+      dma16(src + tp * C::ROWB + ch * 16, dst + u * 1024);
+    }
   }
   if constexpr (FP8) {
-    const int64_t sA = ((int64_t)pid.a * A.num_kv_heads + g) * kBlock + 4 * c;
-    const int64_t sB = ((int64_t)pid.b * A.num_kv_heads + g) * kBlock + 4 * c;
-    R.ks[0] = *reinterpret_cast<const f32x4*>(A.k_scales + sA);
-    R.ks[1] = *reinterpret_cast<const f32x4*>(A.k_scales + sB);
+    if (w == 0) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
+      const int which = lane >> 4, tok = lane & 15;
+      const int pg = __builtin_amdgcn_readfirstlane(sm.pages[2 * k + 1]);
+      const int pgs = (which & 1) ? pg : page;
+      const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
+                          ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
+      dma4(src2, sb + RG::KB + RG::VB);
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// V^T operands for one chunk: all transposing LDS reads of the stage in one
+// asm block that ends with lgkmcnt(0). (The compiler treats the transposing
+// read intrinsics as possibly aliasing any in-flight direct-to-LDS load and
+// would drain every outstanding load before them; the ring's own waits have
+// already made the stage's data visible.) lane_off[mt] is the lane's byte
+// address of the first read of output tile mt; the bf16 reads of tokens
+// 16..31 sit 16 token rows further.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+#define PAV_TR16_PAIR(i, off) "ds_read_b64_tr_b16 %" #i ", %[a" #off "]\n\t"
+
+__device__ __forceinline__ void vt_reads_bf16_d128(s16x4 (&r)[16], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+__device__ __forceinline__ void vt_reads_bf16_d64(s16x4 (&r)[8], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+__device__ __forceinline__ void vt_reads_fp8_d128(i32x2 (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %8\n\t"
+      "ds_read_b64_tr_b8 %1, %9\n\t"
+      "ds_read_b64_tr_b8 %2, %10\n\t"
+      "ds_read_b64_tr_b8 %3, %11\n\t"
+      "ds_read_b64_tr_b8 %4, %12\n\t"
+      "ds_read_b64_tr_b8 %5, %13\n\t"
+      "ds_read_b64_tr_b8 %6, %14\n\t"
+      "ds_read_b64_tr_b8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+__device__ __forceinline__ void vt_reads_fp8_d64(i32x2 (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4\n\t"
+      "ds_read_b64_tr_b8 %1, %5\n\t"
+      "ds_read_b64_tr_b8 %2, %6\n\t"
+      "ds_read_b64_tr_b8 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
 }
 
 template <int D, bool FP8>
-__device__ __forceinline__ void load_v(ChunkRegs<D, FP8>& R, const KernelArgs& A, PageIds pid,
-                                       int g, int lane) {
-  using C = Cfg<D, FP8>;
-  const int c = lane >> 4;
-  const char* vp = static_cast<const char*>(A.v_pool);
-  const int64_t baseA = ((int64_t)pid.a * A.num_kv_heads + g) * C::BLKB;
-  const int64_t baseB = ((int64_t)pid.b * A.num_kv_heads + g) * C::BLKB;
-#pragma unroll
-  for (int u = 0; u < C::VLD; ++u) {
-    const int o = u * 1024;
-    const int64_t base = (o / C::BLKB) ? baseB : baseA;
-    R.v[u] = *reinterpret_cast<const u32x4*>(vp + base + (o % C::BLKB) + lane * 16);
-  }
-  if constexpr (FP8) {
-    const int64_t sA = ((int64_t)pid.a * A.num_kv_heads + g) * kBlock + 4 * c;
-    const int64_t sB = ((int64_t)pid.b * A.num_kv_heads + g) * kBlock + 4 * c;
-    R.vs[0] = *reinterpret_cast<const f32x4*>(A.v_scales + sA);
-    R.vs[1] = *reinterpret_cast<const f32x4*>(A.v_scales + sB);
-  }
-}
-
-template <int D, bool FP8, int NT>
 struct WaveState {
-  bf16x8 q[NT][Cfg<D, FP8>::KS];
-  f32x4 o[Cfg<D, FP8>::MT][NT];
-  float m[NT];   // reference max per row (log2 units); p <= 2^kRescale
-  float l[NT];   // this lane's share of the row sum
-  int prow[NT];  // absolute position of the lane's row (row = 16 nt + lane % 16)
+  bf16x8 q[Cfg<D, FP8>::KS];
+  f32x4 o[Cfg<D, FP8>::MT];
+  float m;   // reference max of the lane's row (log2 units); p <= 2^kRescale
+  float l;   // this lane's share of the row sum
+  int prow;  // absolute position of the lane's row
 };
 
 // The reference max only moves when a chunk's max exceeds it by more than
-// this many log2 units; until then probabilities stay below 2^8, and the
-// accumulators are rescaled rarely. The result is the same up to rounding:
-// O, l and m always refer to one common reference.
+// this many log2 units; until then probabilities stay below 2^8 and the
+// accumulators are not rescaled. O, l and m always share one reference.
 constexpr float kRescale = 8.0f;
 
-// One 32-token chunk: QK, the next chunk's loads, mask, online softmax, PV.
-template <int D, bool FP8, int NT>
-__device__ __forceinline__ void process_chunk(WaveState<D, FP8, NT>& S, ChunkRegs<D, FP8>& R,
-                                              unsigned char* vt, const KernelArgs& A,
-                                              const int32_t* bt, int g, int tok0, int next_tok0,
-                                              int tv0, int tv1, int L, int q, int W, int lane) {
+// One chunk for the wave's 16-row tile, from ring stage `sb`.
+template <int D, bool FP8>
+__device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsigned char* sb,
+                                              int tok0, int tv0, int tv1, int L, int q, int W,
+                                              float scale_log2, int lane) {
   using C = Cfg<D, FP8>;
-  const int n = lane & 15, c = lane >> 4;
-  const float scale_log2 = A.scale_log2;
+  using RG = Ring<D, FP8>;
+  const int c = lane >> 4;
+  const int i16 = lane & 15;
 
-  // ---- S^T = K Q^T: tokens of each page on M, packed rows on N.
-  f32x4 sc[2][NT];
+  // ---- LDS reads of the stage: K operands, then every V^T operand (one
+  // asm block whose lgkmcnt(0) also covers the K reads), so both latencies
+  // overlap.
+  u32x4 kr[2][C::KLD];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int u = 0; u < C::KLD; ++u)
+      kr[bb][u] = *reinterpret_cast<const u32x4*>(sb + (bb * C::KLD + u) * 1024 + lane * 16);
+  f32x4 ksc[2], vs[2];
+  if constexpr (FP8) {
+    const unsigned char* scl = sb + RG::KB + RG::VB;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      ksc[bb] = *reinterpret_cast<const f32x4*>(scl + (bb * 16 + 4 * c) * 4);
+      vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
+    }
+  }
+  const uint32_t vt = lds_addr(sb + RG::KB);
+  uint32_t va[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) {
+    if constexpr (FP8) {
+      const int r = i16 >> 1, k = i16 & 1;
+      const int t = 16 * (r >> 2) + 4 * c + (r & 3);
+      va[mt] = vt + vtile_chunk<D, FP8>(t, mt) + 8 * k;
+    } else {
+      const int r = i16 >> 2, k = i16 & 3;
+      va[mt] = vt + vtile_chunk<D, FP8>(4 * c + r, 2 * mt + (k >> 1)) + 8 * (k & 1);
+    }
+  }
+  bf16x8 vops[C::MT];
+  if constexpr (FP8) {
+    i32x2 codes[C::MT];
+    if constexpr (D == 128) vt_reads_fp8_d128(codes, va);
+    else vt_reads_fp8_d64(codes, va);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      vops[mt] = fp8x8_to_bf16((uint32_t)codes[mt][0], (uint32_t)codes[mt][1]);
+  } else {
+    s16x4 rd[2 * C::MT];
+    if constexpr (D == 128) vt_reads_bf16_d128(rd, va);
+    else vt_reads_bf16_d64(rd, va);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      vops[mt] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(rd[2 * mt], rd[2 * mt + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // ---- S^T = K Q^T: the two pages' tokens on M, the tile's rows on N.
+  f32x4 sc[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    bf16x8 kop[C::KS];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u) {
       if constexpr (FP8) {
-        kop[2 * u] = fp8x8_to_bf16(R.k[bb][u][0], R.k[bb][u][1]);
-        kop[2 * u + 1] = fp8x8_to_bf16(R.k[bb][u][2], R.k[bb][u][3]);
+        acc = mfma_bf16(fp8x8_to_bf16(kr[bb][u][0], kr[bb][u][1]), S.q[2 * u], acc);
+        acc = mfma_bf16(fp8x8_to_bf16(kr[bb][u][2], kr[bb][u][3]), S.q[2 * u + 1], acc);
       } else {
-        kop[u] = __builtin_bit_cast(bf16x8, R.k[bb][u]);
+        acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[bb][u]), S.q[u], acc);
       }
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) acc = mfma_bf16(kop[s], S.q[nt][s], acc);
-      sc[bb][nt] = acc;
-    }
-  }
-  if constexpr (FP8) {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[bb][nt] *= R.ks[bb];
-  }
-  // K registers are free: start the next chunk's K loads.
-  const bool has_next = next_tok0 >= 0;
-  PageIds nxt{0, 0};
-  if (has_next) {
-    nxt = page_ids(bt, next_tok0, tv1);
-    load_k<D, FP8>(R, A, nxt, g, lane);
+    sc[bb] = FP8 ? acc * ksc[bb] : acc;
   }
 
-  // Chunks wholly inside every row's visible range skip the mask.
+  // ---- Masks, only for chunks not wholly inside every row's visible range:
+  // scores of invisible keys become -inf; V^T entries (and FP8 V scales) of
+  // tokens outside the item's valid range become 0, since their pool slots
+  // may hold anything, NaN included.
   const bool fast = (tok0 >= tv0) && (tok0 + kChunk <= tv1) && (tok0 + kChunk - 1 <= L - q) &&
                     (W == 0 || tok0 > L - 1 - W);
-
-  // ---- V: registers -> swizzled LDS tile (invalid tokens zeroed).
-  f32x4 vs[2];
-  if constexpr (FP8) {
-    vs[0] = R.vs[0];
-    vs[1] = R.vs[1];
-  }
-#pragma unroll
-  for (int u = 0; u < C::VLD; ++u) {
-    const int o = u * 1024 + lane * 16;
-    const int bb = o / C::BLKB;
-    const int ob = o % C::BLKB;
-    const int t = 16 * bb + ob / C::ROWB;  // token within the chunk
-    const int ch = (ob % C::ROWB) >> 4;    // 16-byte chunk within the token row
-    const int j = tok0 + t;
-    u32x4 val = R.v[u];
-    if (!fast && !((j >= tv0) && (j < tv1))) val = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(vt + vtile_chunk<D, FP8>(t, ch)) = val;
-  }
-  // V registers are free: start the next chunk's V loads.
-  if (has_next) load_v<D, FP8>(R, A, nxt, g, lane);
-
   if (!fast) {
+    const int p = S.prow;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = tok0 + 16 * bb + 4 * c + i;
-        const bool tok_ok = (j >= tv0) && (j < tv1);
-        if constexpr (FP8) vs[bb][i] = tok_ok ? vs[bb][i] : 0.f;
+        const bool ok = (j >= tv0) && (j < tv1);
+        const bool vis = ok && (j <= p) && (W == 0 || j > p - W);
+        sc[bb][i] = vis ? sc[bb][i] : -INFINITY;
+        if constexpr (FP8) vs[bb][i] = ok ? vs[bb][i] : 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int p = S.prow[nt];
-          const bool vis = tok_ok && (j <= p) && (W == 0 || j > p - W);
-          sc[bb][nt][i] = vis ? sc[bb][nt][i] : -INFINITY;
-        }
+        for (int mt = 0; mt < C::MT; ++mt)
+          vops[mt][4 * bb + i] = ok ? vops[mt][4 * bb + i] : (__bf16)0.f;
       }
     }
   }
 
   // ---- Online softmax in the exp2 domain (x = s * sigma * log2 e).
-  float mx[NT];
-  bool grow = false;
+  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  mx = xlane_max4(mx) * scale_log2;
+  if (__any(mx > S.m + kRescale)) {
+    const float mnew = fmaxf(S.m, mx);
+    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
+    S.m = mnew;
+    S.l *= alpha;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float v = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
-                    fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
-    mx[nt] = xlane_max4(v) * scale_log2;
-    grow |= mx[nt] > S.m[nt] + kRescale;
-  }
-  if (__any(grow)) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mnew = fmaxf(S.m[nt], mx[nt]);
-      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m[nt] - mnew);
-      S.m[nt] = mnew;
-      S.l[nt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) S.o[mt][nt] *= alpha;
-    }
+    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] *= alpha;
   }
   // P enters the PV product as two bf16 terms, hi = bf16(p) and
   // lo = bf16(p - hi), so its rounding error (about 2^-17 relative) stays far
   // below the output's own bf16 rounding even when one key dominates a row.
-  bf16x8 pop_hi[NT], pop_lo[NT];
+  const float msafe = (S.m == -INFINITY) ? 0.f : S.m;
+  bf16x8 p_hi, p_lo;
+  float ps = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float msafe = (S.m[nt] == -INFINITY) ? 0.f : S.m[nt];
-    float ps = 0.f;
+  for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sc[bb][nt][i], scale_log2, -msafe));
-        ps += p;
-        const float pw = FP8 ? p * vs[bb][i] : p;
-        const __bf16 hi = (__bf16)pw;
-        pop_hi[nt][4 * bb + i] = hi;
-        pop_lo[nt][4 * bb + i] = (__bf16)(pw - (float)hi);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(sc[bb][i], scale_log2, -msafe));
+      ps += p;
+      const float pw = FP8 ? p * vs[bb][i] : p;
+      const __bf16 hi = (__bf16)pw;
+      p_hi[4 * bb + i] = hi;
+      p_lo[4 * bb + i] = (__bf16)(pw - (float)hi);
     }
-    S.l[nt] += ps;
   }
-
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  S.l += ps;
 
   // ---- O^T[d][row] += V^T[d][token] P^T[token][row]. The contraction index
   // (lane group c, element e) is token 16 (e / 4) + 4 c + e % 4 for both
   // operands: that is where the S^T accumulator left P.
-  const int i16 = lane & 15;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
-    bf16x8 vop;
-    if constexpr (FP8) {
-      const int r = i16 >> 1, k = i16 & 1;
-      const int t = 16 * (r >> 2) + 4 * c + (r & 3);
-      const i32x2 codes = lds_tr8(vt, vtile_chunk<D, FP8>(t, mt) + 8 * k);
-      vop = fp8x8_to_bf16((uint32_t)codes[0], (uint32_t)codes[1]);
-    } else {
-      const int r = i16 >> 2, k = i16 & 3;
-      const int t0 = 4 * c + r;
-      const int ch = 2 * mt + (k >> 1);
-      const s16x4 lo = lds_tr16(vt, vtile_chunk<D, FP8>(t0, ch) + 8 * (k & 1));
-      const s16x4 hi = lds_tr16(vt, vtile_chunk<D, FP8>(t0 + 16, ch) + 8 * (k & 1));
-      vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      S.o[mt][nt] = mfma_bf16(vop, pop_hi[nt], S.o[mt][nt]);
-      S.o[mt][nt] = mfma_bf16(vop, pop_lo[nt], S.o[mt][nt]);
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  (void)n;
-}
-
-template <int D, bool FP8, int NT>
-__device__ __forceinline__ void run_item(const KernelArgs& A, const WorkItem& it,
-                                         const SeqInfo& si, Smem& sm) {
-  using C = Cfg<D, FP8>;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int n = lane & 15, c = lane >> 4;
-  const int b = it.seq, g = it.kv_head;
-  const int G = A.group, Hq = A.num_q_heads;
-  const int L = si.ctx_len, q = si.q_len, W = si.window;
-  const int rows = q * G;
-  const int tv0 = it.key_begin, tv1 = it.key_end;
-
-  WaveState<D, FP8, NT> S;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = 16 * nt + n;
-    const bool live = row < rows;
-    const int rr = live ? row : rows - 1;  // padding rows mirror the last real row
-    const int i = rr / G, hh = rr % G;
-    S.prow[nt] = L - q + i;
-    S.m[nt] = -INFINITY;
-    S.l[nt] = 0.f;
-    const uint16_t* qp = A.q + ((int64_t)(si.q_off + i) * Hq + g * G + hh) * D;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4 v = {0, 0, 0, 0};
-      if (live) v = *reinterpret_cast<const u32x4*>(qp + qk_dmap<D, FP8>(s, c));
-      S.q[nt][s] = __builtin_bit_cast(bf16x8, v);
-    }
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  unsigned char* vt = reinterpret_cast<unsigned char*>(&sm.buf[0][0][0]) +
-                      w * (kChunk * D * (FP8 ? 1 : 2));
-  const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
-  const int tokbase = (tv0 >> 4) << 4;
-  const int nch = (tv1 - tokbase + kChunk - 1) / kChunk;
-
-  // One chunk of look-ahead: the next chunk's K is requested as soon as the
-  // current K has been consumed by the MFMAs, its V once the current V sits
-  // in LDS.
-  ChunkRegs<D, FP8> R;
-  if (w < nch) {
-    const PageIds pid = page_ids(bt, tokbase + w * kChunk, tv1);
-    load_k<D, FP8>(R, A, pid, g, lane);
-    load_v<D, FP8>(R, A, pid, g, lane);
-  }
-  for (int ci = w; ci < nch; ci += kWaves) {
-    const int next = ci + kWaves < nch ? tokbase + (ci + kWaves) * kChunk : -1;
-    process_chunk<D, FP8, NT>(S, R, vt, A, bt, g, tokbase + ci * kChunk, next, tv0, tv1, L, q, W,
-                              lane);
-  }
-
-  // ---- Merge the four waves' states.
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) S.l[nt] = xlane_sum4(S.l[nt]);
-  __syncthreads();  // every wave is done with its V tile (aliases buf)
-  if (c == 0) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sm.ml[w][16 * nt + n] = make_float2(S.m[nt], S.l[nt]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = 16 * nt + n;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm.ml[v][row].x);
-    const float f = (S.m[nt] == -INFINITY) ? 0.f : fast_exp2(S.m[nt] - M);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      *reinterpret_cast<f32x4*>(&sm.buf[w][row][16 * mt + 4 * c]) = S.o[mt][nt] * f;
-  }
-  __syncthreads();
-
-  // ---- Epilogue: all 256 threads, 4 consecutive d per thread.
-  constexpr int D4 = D / 4;
-  for (int e = tid; e < rows * D4; e += kThreads) {
-    const int row = e / D4;
-    const int d = (e % D4) * 4;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm.ml[v][row].x);
-    float Ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float2 ml = sm.ml[v][row];
-      Ls += (ml.x == -INFINITY) ? 0.f : ml.y * fast_exp2(ml.x - M);
-    }
-    f32x4 acc = *reinterpret_cast<const f32x4*>(&sm.buf[0][row][d]);
-#pragma unroll
-    for (int v = 1; v < kWaves; ++v) acc += *reinterpret_cast<const f32x4*>(&sm.buf[v][row][d]);
-    const int i = row / G, hh = row % G;
-    const int h = g * G + hh;
-    if (it.slot < 0) {
-      float zs = -INFINITY;
-      if (A.sinks_mode == 1) zs = A.sinks[h] * kLog2e;
-      else if (A.sinks_mode == 2) zs = A.sinks[(int64_t)b * Hq + h] * kLog2e;
-      const float Mx = fmaxf(M, zs);
-      const float a = fast_exp2(M - Mx);
-      const float den = Ls * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
-      acc *= a / den;
-      const int64_t oi = ((int64_t)(si.q_off + i) * Hq + h) * D + d;
-      if (A.out_fp32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + oi) = acc;
-      } else {
-        bf16x2 p0 = {(__bf16)acc[0], (__bf16)acc[1]};
-        bf16x2 p1 = {(__bf16)acc[2], (__bf16)acc[3]};
-        uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-        *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + oi) = pk;
-      }
-    } else {
-      const int64_t pr = (int64_t)it.slot * A.rows_stride + row;
-      *reinterpret_cast<f32x4*>(A.part_o + pr * D + d) = acc;
-      if (d == 0) *reinterpret_cast<float2*>(A.part_ml + pr * 2) = make_float2(M, Ls);
-    }
+    S.o[mt] = mfma_bf16(vops[mt], p_hi, S.o[mt]);
+    S.o[mt] = mfma_bf16(vops[mt], p_lo, S.o[mt]);
   }
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A) {
+__global__ __launch_bounds__(kThreads, 3) void pa_partition_kernel(KernelArgs A) {
+  using C = Cfg<D, FP8>;
+  using RG = Ring<D, FP8>;
   __shared__ Smem sm;
   const WorkItem it = A.items[blockIdx.x];
-  const SeqInfo si = A.seqs[it.seq];
-  const int rows = si.q_len * A.group;
-  switch ((rows + 15) >> 4) {
-    case 1: run_item<D, FP8, 1>(A, it, si, sm); break;
-    case 2: run_item<D, FP8, 2>(A, it, si, sm); break;
-    case 3: run_item<D, FP8, 3>(A, it, si, sm); break;
-    default: run_item<D, FP8, 4>(A, it, si, sm); break;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int n = lane & 15, c = lane >> 4;
+  const int b = it.seq, g = it.kv_head;
+  const int G = A.group, Hq = A.num_q_heads;
+  const int L = it.ctx_len, q = it.q_len, W = it.window;
+  const int rows = q * G;
+  const int nt = (rows + 15) >> 4;  // row tiles; waves w >= nt only load
+  const bool active = w < nt;
+  const int tv0 = it.key_begin, tv1 = it.key_end;
+  const int tokbase = (tv0 >> 4) << 4;
+  const int nch = (tv1 - tokbase + kChunk - 1) / kChunk;
+
+  // Page ids of every chunk (a page past the item's end repeats the last
+  // one, whose slots the masks then exclude).
+  const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
+  for (int i = tid; i < 2 * nch; i += kThreads) {
+    const int k = i >> 1, which = i & 1;
+    const int tok0 = tokbase + k * kChunk;
+    const int pg = (tok0 >> 4) + which;
+    sm.pages[i] = bt[(which == 0 || tok0 + kBlock < tv1) ? pg : pg - 1];
+  }
+
+  // The wave's row tile: row = 16 w + lane % 16 (padding rows mirror the
+  // last real row and carry a zero query).
+  WaveState<D, FP8> S;
+  {
+    const int row = 16 * w + n;
+    const bool live = active && row < rows;
+    const int rr = live ? row : rows - 1;
+    const int i = rr / G, hh = rr % G;
+    S.prow = L - q + i;
+    S.m = -INFINITY;
+    S.l = 0.f;
+    const uint16_t* qp = A.q + ((int64_t)(it.q_off + i) * Hq + g * G + hh) * D;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      u32x4 v = {0, 0, 0, 0};
+      if (live) v = *reinterpret_cast<const u32x4*>(qp + qk_dmap<D, FP8>(s, c));
+      S.q[s] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Finish the query and table loads here, with a wait the compiler sees:
+  // otherwise it waits for the query inside the chunk loop, where vmcnt(0)
+  // would also drain the ring's loads on every chunk.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
+  __syncthreads();  // page ids visible to every wave
+
+  // Fill the first R - 1 stages; then per chunk: wait for this wave's loads
+  // of it, barrier (everyone's loads have landed and everyone is done with
+  // the stage about to be refilled), refill that stage, compute.
+  for (int k = 0; k < RG::R - 1 && k < nch; ++k)
+    issue_chunk<D, FP8>(A, sm, sm.ring + k * RG::STAGE, k, g, w, lane);
+  for (int k = 0; k < nch; ++k) {
+    if (k + RG::R - 2 < nch) {
+      if (FP8 && w == 0) wait_vm<RG::WAIT0>();
+      else wait_vm<RG::WAIT>();
+    } else {
+      wait_vm<0>();
+    }
+    ring_barrier();
+    if (k + RG::R - 1 < nch)
+      issue_chunk<D, FP8>(A, sm, sm.ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, k + RG::R - 1,
+                          g, w, lane);
+    if (active)
+      compute_chunk<D, FP8>(S, sm.ring + (k % RG::R) * RG::STAGE, tokbase + k * kChunk, tv0, tv1,
+                            L, q, W, A.scale_log2, lane);
+  }
+  if (!active) return;
+
+  // ---- Epilogue: the wave writes its rows (lane: row n, d = 16 mt + 4 c + i).
+  S.l = xlane_sum4(S.l);
+  const int row = 16 * w + n;
+  if (row >= rows) return;
+  const int i = row / G, hh = row % G;
+  const int h = g * G + hh;
+  if (it.slot < 0) {
+    float zs = -INFINITY;
+    if (A.sinks_mode == 1) zs = A.sinks[h] * kLog2e;
+    else if (A.sinks_mode == 2) zs = A.sinks[(int64_t)b * Hq + h] * kLog2e;
+    const float Mx = fmaxf(S.m, zs);
+    const float a = fast_exp2(S.m - Mx);
+    const float den = S.l * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
+    const float r = a / den;
+    const int64_t ob = ((int64_t)(it.q_off + i) * Hq + h) * D + 4 * c;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const f32x4 v = S.o[mt] * r;
+      if (A.out_fp32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + ob + 16 * mt) = v;
+      } else {
+        bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
+        bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
+        uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+        *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + ob + 16 * mt) = pk;
+      }
+    }
+  } else {
+    const int64_t pr = (int64_t)it.slot * A.rows_stride + row;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      *reinterpret_cast<f32x4*>(A.part_o + pr * D + 16 * mt + 4 * c) = S.o[mt];
+    if (c == 0) *reinterpret_cast<float2*>(A.part_ml + pr * 2) = make_float2(S.m, S.l);
   }
 }
 
 // Log-sum-exp merge of the partials of one (sequence, KV head):
 //   M = max(max_k m_k, z), Z = sum_k l_k 2^(m_k - M) + 2^(z - M),
 //   out = sum_k 2^(m_k - M) O_k / Z       (all in log2 units).
-// Grid: one workgroup per (reduce item, group of rows); D/4 threads per row.
+// Grid: (reduce item, row, quarter of D); 256 threads = 8 column lanes (4
+// values each) x 32 partition lanes, so a row's partials are read 32 at a
+// time and no thread walks more than n_parts / 32 of them. The partition
+// lanes combine through LDS in a fixed order.
+constexpr int kRedCols = 8;
+constexpr int kRedParts = 256 / kRedCols;
+
 template <int D>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
-  constexpr int TPR = D / 4;
-  constexpr int RPW = 256 / TPR;
-  constexpr int GROUPS = (kMaxRows + RPW - 1) / RPW;
-  const ReduceItem ri = A.red[blockIdx.x / GROUPS];
-  const int rg = blockIdx.x % GROUPS;
+  constexpr int DSPLIT = D / 4 / kRedCols;
+  __shared__ float s_m[kRedParts];
+  __shared__ float s_z[kRedParts];
+  __shared__ f32x4 s_o[kRedParts][kRedCols];
+  const int bid = blockIdx.x;
+  const int ds = bid % DSPLIT;
+  const int row = (bid / DSPLIT) % kMaxRows;
+  const ReduceItem ri = A.red[bid / (DSPLIT * kMaxRows)];
   const SeqInfo si = A.seqs[ri.seq];
   const int G = A.group, Hq = A.num_q_heads;
   const int rows = si.q_len * G;
-  const int row = rg * RPW + threadIdx.x / TPR;
-  if (row >= rows) return;
-  const int d = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;  // uniform over the workgroup
+  const int dl = threadIdx.x % kRedCols, pl = threadIdx.x / kRedCols;
+  const int d = (ds * kRedCols + dl) * 4;
+  const int n = ri.n_parts;
+  const float* ml = A.part_ml + ((int64_t)ri.slot_base * A.rows_stride + row) * 2;
+  const float* po = A.part_o + ((int64_t)ri.slot_base * A.rows_stride + row) * D + d;
+  const int64_t mstride = (int64_t)A.rows_stride * 2;
+  const int64_t ostride = (int64_t)A.rows_stride * D;
+
+  float m = -INFINITY;
+#pragma unroll 4
+  for (int k = pl; k < n; k += kRedParts) m = fmaxf(m, ml[k * mstride]);
+  if (dl == 0) s_m[pl] = m;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int j = 0; j < kRedParts; ++j) M = fmaxf(M, s_m[j]);
+  float zs = -INFINITY;
   const int i = row / G, hh = row % G;
   const int h = ri.kv_head * G + hh;
-  float M = -INFINITY;
-  for (int k = 0; k < ri.n_parts; ++k) {
-    const int64_t pr = (int64_t)(ri.slot_base + k) * A.rows_stride + row;
-    M = fmaxf(M, A.part_ml[pr * 2]);
-  }
-  float zs = -INFINITY;
   if (A.sinks_mode == 1) zs = A.sinks[h] * kLog2e;
   else if (A.sinks_mode == 2) zs = A.sinks[(int64_t)ri.seq * Hq + h] * kLog2e;
   const float Mx = fmaxf(M, zs);
-  float Z = (zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx);
+
+  float z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < ri.n_parts; ++k) {
-    const int64_t pr = (int64_t)(ri.slot_base + k) * A.rows_stride + row;
-    const float2 ml = *reinterpret_cast<const float2*>(A.part_ml + pr * 2);
-    if (ml.x == -INFINITY) continue;  // a partition no key of which this row sees
-    const float wk = fast_exp2(ml.x - Mx);
-    Z += ml.y * wk;
-    acc += *reinterpret_cast<const f32x4*>(A.part_o + pr * D + d) * wk;
+#pragma unroll 4
+  for (int k = pl; k < n; k += kRedParts) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + k * mstride);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(po + k * ostride);
+    const float wk = (v.x == -INFINITY) ? 0.f : fast_exp2(v.x - Mx);
+    z += v.y * wk;
+    acc += o * wk;
   }
-  acc *= 1.0f / Z;
+  if (dl == 0) s_z[pl] = z;
+  s_o[pl][dl] = acc;
+  __syncthreads();
+  if (pl != 0) return;
+  float Z = (zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx);
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kRedParts; ++j) {
+    Z += s_z[j];
+    tot += s_o[j][dl];
+  }
+  tot *= 1.0f / Z;
   const int64_t oi = ((int64_t)(si.q_off + i) * Hq + h) * D + d;
   if (A.out_fp32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + oi) = acc;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + oi) = tot;
   } else {
-    bf16x2 p0 = {(__bf16)acc[0], (__bf16)acc[1]};
-    bf16x2 p1 = {(__bf16)acc[2], (__bf16)acc[3]};
+    bf16x2 p0 = {(__bf16)tot[0], (__bf16)tot[1]};
+    bf16x2 p1 = {(__bf16)tot[2], (__bf16)tot[3]};
     uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
     *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + oi) = pk;
   }
@@ -587,11 +707,13 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, hipStream
   if (n_red <= 0) return hipSuccess;
   dim3 block(256);
   if (head_dim == 128) {
-    constexpr int groups = kMaxRows / (256 / 32);
-    hipLaunchKernelGGL((pa_reduce_kernel<128>), dim3(n_red * groups), block, 0, stream, a);
+    constexpr int split = 128 / 4 / kRedCols;
+    hipLaunchKernelGGL((pa_reduce_kernel<128>), dim3(n_red * kMaxRows * split), block, 0, stream,
+                       a);
   } else {
-    constexpr int groups = kMaxRows / (256 / 16);
-    hipLaunchKernelGGL((pa_reduce_kernel<64>), dim3(n_red * groups), block, 0, stream, a);
+    constexpr int split = 64 / 4 / kRedCols;
+    hipLaunchKernelGGL((pa_reduce_kernel<64>), dim3(n_red * kMaxRows * split), block, 0, stream,
+                       a);
   }
   return hipGetLastError();
 }

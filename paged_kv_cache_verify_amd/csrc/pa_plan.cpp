@@ -110,6 +110,9 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
   if (s->partition_tokens < 0 || s->partition_tokens % kBlock != 0)
     return fail(PA_E_INVALID, "partition_tokens %d must be 0 or a positive multiple of 16",
                 s->partition_tokens);
+  if (s->partition_tokens > kMaxItemKeys)
+    return fail(PA_E_UNSUPPORTED, "partition_tokens %d exceeds the %d keys a work item spans",
+                s->partition_tokens, kMaxItemKeys);
   if (s->sinks_mode < 0 || s->sinks_mode > 2)
     return fail(PA_E_INVALID, "sinks_mode %d is not 0, 1 or 2", s->sinks_mode);
   const int G = s->num_q_heads / s->num_kv_heads;
@@ -151,7 +154,7 @@ int32_t auto_partition(int64_t total_keys) {
   int64_t p = (total_keys + target_items - 1) / target_items;
   p = ((p + kChunk - 1) / kChunk) * kChunk;
   p = std::max<int64_t>(p, 256);
-  p = std::min<int64_t>(p, 1 << 16);
+  p = std::min<int64_t>(p, kMaxItemKeys);
   return (int32_t)p;
 }
 
@@ -225,6 +228,10 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
           it.key_begin = std::max(si.lo, a + k * P);
           it.key_end = std::min(si.ctx_len, a + (k + 1) * P);
           it.slot = si.n_parts > 1 ? (int32_t)(si.slot_base + (int64_t)g * si.n_parts + k) : -1;
+          it.ctx_len = si.ctx_len;
+          it.q_len = si.q_len;
+          it.q_off = si.q_off;
+          it.window = si.window;
           p->items.push_back(it);
         }
         if (si.n_parts > 1) {
@@ -233,7 +240,16 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
         }
       }
     }
-    if (p->items.size() >= (size_t)INT32_MAX || p->red.size() * 8 >= (size_t)INT32_MAX) {
+    for (const WorkItem& it : p->items) {
+      // A wave holds the page ids of its chunks in one register (64 lanes).
+      const int span = it.key_end - (it.key_begin / kBlock) * kBlock;
+      if ((span + kChunk - 1) / kChunk > 64 * kWaves) {
+        delete p;
+        return fail(PA_E_UNSUPPORTED, "a work item spans more than %d keys", kMaxItemKeys);
+      }
+    }
+    if (p->items.size() >= (size_t)INT32_MAX ||
+        p->red.size() * kMaxRows * 4 >= (size_t)INT32_MAX) {
       delete p;
       return fail(PA_E_UNSUPPORTED, "the work list exceeds a 1-D grid");
     }

@@ -62,6 +62,8 @@ REFUSALS = [
     (dict(partition_tokens=100), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
     (dict(partition_tokens=-16), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
     (dict(sinks_mode=3), [100, 50], [6, 6], None, pav.PA_E_INVALID, "sinks_mode"),
+    (dict(partition_tokens=8192 + 16), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED,
+     "work item"),
     ({}, [100, 50], [9, 6], None, pav.PA_E_UNSUPPORTED, "verify limit"),
     ({}, [100, 50], [-1, 6], None, pav.PA_E_INVALID, "< 0"),
     ({}, [5, 50], [6, 6], None, pav.PA_E_INVALID, "smaller than its query"),
@@ -150,7 +152,7 @@ def check_worklist(plan, ctx, q, win, Hkv, P=None):
     return items
 
 
-@pytest.mark.parametrize("P", [0, 16, 64, 512, 4096])
+@pytest.mark.parametrize("P", [0, 16, 64, 512, 4096, 8192])
 def test_worklist_tiles_visible_keys(P):
     ctx = [37, 100, 4096, 17, 8, 20000, 1]
     q = [1, 3, 6, 8, 0, 5, 1]
