@@ -8,25 +8,26 @@
 namespace pav {
 
 constexpr int kBlock = 16;      // tokens per KV block
-constexpr int kChunk = 32;      // tokens one wave consumes per iteration (two blocks)
-constexpr int kWaves = 4;       // waves per workgroup; each takes every 4th chunk
-constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 32;      // tokens a wave consumes per iteration (two blocks)
 constexpr int kMaxRows = 64;    // q x G packed rows per KV head (4 MFMA row tiles)
 constexpr int kMaxQuery = 8;
 constexpr int kMaxContext = 1 << 20;
-// Keys per work item: each wave keeps the page ids of its (at most 64)
-// chunks in one register, one chunk per lane.
-constexpr int kMaxItemKeys = 64 * kWaves * kChunk;  // 8192
+// Keys a work item spans from its page-aligned start; the workgroup keeps
+// the page ids of its (at most 256) chunks in LDS.
+constexpr int kMaxItemKeys = 8192;
+constexpr int kMaxItemChunks = kMaxItemKeys / kChunk;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // One workgroup's share of the work: the keys [key_begin, key_end) of one
-// (sequence, KV head). slot < 0 means the item covers all of the pair's
-// visible keys and writes the final output itself.
+// (sequence, KV head), all its q x G rows.
 struct WorkItem {
   int32_t seq;
   int32_t kv_head;
   int32_t key_begin;
   int32_t key_end;
+  // slot < 0: the item covers all of the pair's visible keys and writes the
+  // output itself; otherwise it writes partial `slot`, which the reduce
+  // kernel merges with the pair's other partials.
   int32_t slot;
   // the sequence's fields, repeated here so one load brings everything
   int32_t ctx_len;
@@ -36,23 +37,16 @@ struct WorkItem {
   int32_t pad[7];
 };
 
-struct SeqInfo {
-  int32_t ctx_len;   // L
-  int32_t q_len;     // q (0: padded slot)
-  int32_t q_off;     // first query row of this sequence in q/out
-  int32_t lo;        // first key any row may see (window), else 0
-  int32_t window;    // W, 0 = none
-  int32_t n_parts;   // work items per KV head
-  int32_t slot_base; // partial slot of (kv head 0, part 0) when n_parts > 1
-  int32_t pad;
-};
-
-// A (sequence, KV head) whose partials the reduce kernel merges.
+// A split (sequence, KV head) whose partials [slot_base, slot_base +
+// n_parts) the reduce kernel merges.
 struct ReduceItem {
   int32_t seq;
   int32_t kv_head;
   int32_t slot_base;
   int32_t n_parts;
+  int32_t q_len;
+  int32_t q_off;
+  int32_t pad[2];
 };
 
 struct KernelArgs {
@@ -64,10 +58,9 @@ struct KernelArgs {
   const float* v_scales;
   const float* sinks;
   void* out;
-  float* part_o;   // [slots][rows_stride][D]
-  float* part_ml;  // [slots][rows_stride][2]: running max (log2 units), sum
+  float* part_o;     // [slots][rows_stride][D]
+  float* part_ml;    // [slots][rows_stride][2]: max (log2 units), sum
   const WorkItem* items;
-  const SeqInfo* seqs;
   const ReduceItem* red;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -79,8 +72,12 @@ struct KernelArgs {
   float scale_log2;  // softmax scale x log2(e)
 };
 
-hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8,
+// ntmax: row tiles of 16 the kernel is built for (ceil(max q x G / 16));
+// items with fewer rows skip the missing tiles. One workgroup per CU.
+hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             hipStream_t stream);
-hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, hipStream_t stream);
+// rows_stride: the most rows any reduce item has.
+hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
+                         hipStream_t stream);
 
 }  // namespace pav

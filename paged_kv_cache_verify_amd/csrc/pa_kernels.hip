@@ -1,24 +1,27 @@
 // gfx950 kernels for paged verify attention.
 //
-// Partition kernel: one workgroup (4 waves) per work item = the keys
-// [key_begin, key_end) of one (sequence, KV head), all q x G packed rows of
-// that KV head. The item's keys stream through an LDS ring of R stages, one
-// 32-token chunk (two 16-token pages) per stage, filled by direct
-// global-to-LDS loads that the four waves issue together (K in MFMA
-// A-operand order, V into an XOR-swizzled token-major tile); one barrier per
-// chunk recycles a stage. Each wave owns one tile of 16 rows and, per chunk,
+// Partition kernel: one workgroup of eight waves per work item (and per
+// CU) = the keys [key_begin, key_end) of one (sequence, KV head), all q x G
+// packed rows of that KV head. The waves form two token groups of four:
+// group 0 takes the item's even 32-token chunks (two 16-token pages), group
+// 1 the odd ones, each through an LDS ring of its own filled by direct
+// global-to-LDS loads that the group's four waves issue together (K in MFMA
+// A-operand order, V into an XOR-swizzled token-major tile); one workgroup
+// barrier per step recycles a stage in both rings. Within a group, wave r
+// owns row tile r (16 rows) and, per chunk,
 //   1. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, tokens on the M
-//      index (FP8 codes are converted exactly to bf16 first and the per-token
-//      K scale multiplies the scores),
+//      index (FP8 codes are converted exactly to bf16 first and the
+//      per-token K scale multiplies the scores),
 //   2. masks (causal within the query, window, key range) by selecting -inf,
 //   3. runs an online softmax in the exp2 domain whose reference max only
 //      moves when a chunk beats it by 2^8 (rare rescaling),
 //   4. accumulates O^T += V^T P^T: V^T comes from ds_read_b64_tr_b16 (or
 //      _tr_b8 for FP8) on the tile, P^T straight from the S^T accumulator
 //      registers as a bf16 hi+lo pair (the per-token V scale folded in).
-// A wave's state never leaves its registers, so the epilogue writes the
-// output (or this item's partial) directly. The log-sum-exp reduce kernel
-// merges the partials of split (sequence, KV head) pairs.
+// At the end the two groups' states of each tile merge through LDS and the
+// workgroup writes the output, or this item's partial, which the reduce
+// kernel merges with the other partials of a split (sequence, KV head) by
+// log-sum-exp.
 //
 // Sources: ATOM #2843 ("keep MTP-5 decode on FlyDSL pa_decode past the gluon
 // query-length limit", Motivation and Follow-up in aiter: rows = query length
@@ -132,27 +135,23 @@ __device__ __forceinline__ int vtile_chunk(int t, int chunk) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-#define PAV_LDS __attribute__((address_space(3)))
 
+// Transposing LDS reads (issued from asm below):
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4r + k names the 8
 // bytes at (row r, columns 4k..4k+3) of a 4 x 16 tile of 16-bit values, and
 // lane i receives column i (rows 0..3).
-__device__ __forceinline__ s16x4 lds_tr16(const unsigned char* base, int off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((PAV_LDS s16x4*)(base + off));
-}
 // ds_read_b64_tr_b8: lane 2r + k names the 8 bytes at (row r, columns
 // 8k..8k+7) of an 8 x 16 tile of bytes; lane i receives column i (rows 0..7).
-__device__ __forceinline__ i32x2 lds_tr8(const unsigned char* base, int off) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PAV_LDS i32x2*)(base + off));
-}
-
 
 // ---------------------------------------------------------------------------
-// The LDS ring.
+// The LDS rings: one per token group.
 // ---------------------------------------------------------------------------
 
-constexpr int kRingBytes = 48 * 1024;  // per workgroup: three workgroups fit in a CU
-constexpr int kMaxChunks = kMaxItemKeys / kChunk + 1;
+constexpr int kGroups = 2;                 // token groups per workgroup
+constexpr int kGroupWaves = 4;             // waves per group (one per row tile)
+constexpr int kWaves = kGroups * kGroupWaves;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupRingBytes = 64 * 1024; // per group; the workgroup holds a CU's LDS
 
 template <int D, bool FP8>
 struct Ring {
@@ -161,21 +160,25 @@ struct Ring {
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  static constexpr int R = kRingBytes / STAGE;   // stages
+  static constexpr int R0 = kGroupRingBytes / STAGE;
+  static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
   static constexpr int T = 2 * C::KLD + C::VLD;  // 1 KiB loads per chunk
-  static constexpr int TW = T / kWaves;          // ... issued by each wave
-  static_assert(T % kWaves == 0, "every wave issues the same number of loads");
+  static constexpr int TW = T / kGroupWaves;     // ... issued by each wave of the group
+  static_assert(T % kGroupWaves == 0, "every wave issues the same number of loads");
   static_assert(R >= 3, "the ring needs at least three stages");
   // Loads a wave may still have in flight when it starts on a chunk: those
-  // of the next R - 2 chunks (wave 0 also loads the FP8 scales).
+  // of its group's next R - 2 chunks (wave 0 of a group also loads the FP8
+  // scales).
   static constexpr int WAIT = (R - 2) * TW;
   static constexpr int WAIT0 = (R - 2) * (TW + (FP8 ? 1 : 0));
   static_assert(WAIT0 <= 63, "vmcnt holds at most 63");
+  static constexpr int RING = R * STAGE;         // bytes per group
 };
 
-struct __align__(16) Smem {
-  unsigned char ring[kRingBytes];
-  int32_t pages[2 * kMaxChunks];  // page ids of each chunk's two pages
+template <int D, bool FP8>
+struct Smem {
+  unsigned char ring[kGroups][Ring<D, FP8>::RING];
+  int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
 #define PAV_LDS_VOID __attribute__((address_space(3))) void
@@ -210,44 +213,61 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The wave's share of chunk k's loads into stage `sb`. Wave 0 / 1 load K
-// of the chunk's first / second page (KLD loads of 1 KiB, in MFMA operand
-// order: lane l of load u sits at byte 1024 u + 16 l and is what lane l of
-// the MFMA reads back); wave 2 / 3 load V of the first / second page into
-// the swizzled tile (lane l fetches whichever source chunk belongs at its
-// tile position). Wave 0 also loads the FP8 scales.
+// Page ids of chunk k's two pages, read from asm: the compiler would
+// otherwise drain the ring's in-flight loads before an LDS read it cannot
+// tell apart from their destinations.
+__device__ __forceinline__ void chunk_pages(uint32_t pages_addr, int k, int& pa, int& pb) {
+  i32x2 pp;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(pp)
+               : "v"(pages_addr + 8 * k)
+               : "memory");
+  pa = __builtin_amdgcn_readfirstlane(pp[0]);
+  pb = __builtin_amdgcn_readfirstlane(pp[1]);
+}
+
+// The wave's share of one chunk's loads into stage `sb` of its group's
+// ring. Wave r = 0 / 1 of the group loads K of the chunk's first / second
+// page (KLD loads of 1 KiB, in MFMA operand order: lane l of load u sits at
+// byte 1024 u + 16 l and is what lane l of the MFMA reads back); wave 2 / 3
+// loads V of the first / second page into the swizzled tile (lane l
+// fetches whichever source chunk belongs at its tile position). Wave 0 also
+// loads the FP8 scales. The lane's offsets are derived on every call (the
+// empty asm hides that they never change), rather than held in registers
+// across the loop.
 template <int D, bool FP8>
-__device__ __forceinline__ void issue_chunk(const KernelArgs& A, const Smem& sm,
-                                            unsigned char* sb, int k, int g, int w, int lane) {
+__device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* sb, int pa,
+                                            int pb, int g, int r, int lane) {
   using C = Cfg<D, FP8>;
   using RG = Ring<D, FP8>;
   static_assert(RG::TW == C::KLD && 2 * RG::TW == C::VLD, "one page of K or V per wave");
-  const int n = lane & 15, c = lane >> 4;
-  const int half = w & 1;
-  const int page = __builtin_amdgcn_readfirstlane(sm.pages[2 * k + half]);
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int half = r & 1;
+  const int page = half ? pb : pa;
   const int64_t base = ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
-  if (w < 2) {
-    const char* src = static_cast<const char*>(A.k_pool) + base + n * C::ROWB + 16 * c;
+  if (r < 2) {
+    const char* src = static_cast<const char*>(A.k_pool) + base;
+    const uint32_t off = (ln & 15) * C::ROWB + 16 * (ln >> 4);
     unsigned char* dst = sb + half * C::KLD * 1024;
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) dma16(src + 64 * u, dst + u * 1024);
+    for (int u = 0; u < C::KLD; ++u) dma16(src + (off + 64 * u), dst + u * 1024);
   } else {
     const char* src = static_cast<const char*>(A.v_pool) + base;
     unsigned char* dst = sb + RG::KB + half * (C::BLKB);
 #pragma unroll
     for (int u = 0; u < C::VLD / 2; ++u) {
-      const int pos = u * 1024 + lane * 16;  // byte position in this page's half of the tile
-      const int tp = pos / C::ROWB;          // token within the page
-      const int t = 16 * half + tp;          // token within the chunk (sets the swizzle)
+      const int pos = u * 1024 + ln * 16;  // byte position in this page's half of the tile
+      const int tp = pos / C::ROWB;        // token within the page
+      const int t = 16 * half + tp;        // token within the chunk (sets the swizzle)
       const int ch = ((pos % C::ROWB) >> 4) ^ vswz<D, FP8>(t);  // its source chunk
-      dma16(src + tp * C::ROWB + ch * 16, dst + u * 1024);
+      dma16(src + (uint32_t)(tp * C::ROWB + ch * 16), dst + u * 1024);
     }
   }
   if constexpr (FP8) {
-    if (w == 0) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
-      const int which = lane >> 4, tok = lane & 15;
-      const int pg = __builtin_amdgcn_readfirstlane(sm.pages[2 * k + 1]);
-      const int pgs = (which & 1) ? pg : page;
+    if (r == 0) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
+      const int which = ln >> 4, tok = ln & 15;
+      const int pgs = (which & 1) ? pb : pa;
       const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
                           ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
       dma4(src2, sb + RG::KB + RG::VB);
@@ -500,27 +520,47 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads, 3) void pa_partition_kernel(KernelArgs A) {
+__device__ __forceinline__ void store_out(const KernelArgs& A, int64_t idx, f32x4 v) {
+  if (A.out_fp32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + idx) = v;
+  } else {
+    bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
+    bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
+    uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+    *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + idx) = pk;
+  }
+}
+
+__device__ __forceinline__ float sink_log2(const KernelArgs& A, int b, int h) {
+  if (A.sinks_mode == 1) return A.sinks[h] * kLog2e;
+  if (A.sinks_mode == 2) return A.sinks[(int64_t)b * A.num_q_heads + h] * kLog2e;
+  return -INFINITY;
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
   using RG = Ring<D, FP8>;
-  __shared__ Smem sm;
+  __shared__ Smem<D, FP8> sm;
   const WorkItem it = A.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int gp = w / kGroupWaves, r = w % kGroupWaves;     // token group, row tile
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
   const int L = it.ctx_len, q = it.q_len, W = it.window;
   const int rows = q * G;
-  const int nt = (rows + 15) >> 4;  // row tiles; waves w >= nt only load
-  const bool active = w < nt;
+  const int nt = (rows + 15) >> 4;  // row tiles; waves r >= nt only load
+  const bool active = r < nt;
   const int tv0 = it.key_begin, tv1 = it.key_end;
   const int tokbase = (tv0 >> 4) << 4;
-  const int nch = (tv1 - tokbase + kChunk - 1) / kChunk;
+  const int nch = (tv1 - tokbase + kChunk - 1) / kChunk;  // <= kMaxItemChunks
+  const int nst = (nch + kGroups - 1) / kGroups;           // steps: one chunk per group
 
-  // Page ids of every chunk (a page past the item's end repeats the last
-  // one, whose slots the masks then exclude).
+  // Page ids of every chunk (a page past the item's end repeats the
+  // chunk's first page, whose slots the masks then exclude).
   const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
   for (int i = tid; i < 2 * nch; i += kThreads) {
     const int k = i >> 1, which = i & 1;
@@ -529,11 +569,11 @@ __global__ __launch_bounds__(kThreads, 3) void pa_partition_kernel(KernelArgs A)
     sm.pages[i] = bt[(which == 0 || tok0 + kBlock < tv1) ? pg : pg - 1];
   }
 
-  // The wave's row tile: row = 16 w + lane % 16 (padding rows mirror the
+  // The wave's row tile: row = 16 r + lane % 16 (padding rows mirror the
   // last real row and carry a zero query).
   WaveState<D, FP8> S;
   {
-    const int row = 16 * w + n;
+    const int row = 16 * r + n;
     const bool live = active && row < rows;
     const int rr = live ? row : rows - 1;
     const int i = rr / G, hh = rr % G;
@@ -555,56 +595,78 @@ __global__ __launch_bounds__(kThreads, 3) void pa_partition_kernel(KernelArgs A)
   // would also drain the ring's loads on every chunk.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
   __syncthreads();  // page ids visible to every wave
+  const uint32_t pages_addr = lds_addr(sm.pages);
+  unsigned char* ring = sm.ring[gp];
 
-  // Fill the first R - 1 stages; then per chunk: wait for this wave's loads
-  // of it, barrier (everyone's loads have landed and everyone is done with
-  // the stage about to be refilled), refill that stage, compute.
-  for (int k = 0; k < RG::R - 1 && k < nch; ++k)
-    issue_chunk<D, FP8>(A, sm, sm.ring + k * RG::STAGE, k, g, w, lane);
-  for (int k = 0; k < nch; ++k) {
-    if (k + RG::R - 2 < nch) {
-      if (FP8 && w == 0) wait_vm<RG::WAIT0>();
+  // Chunk of this wave's group at step k: gp + 2 k. Fill the first R - 1
+  // stages; then per step: wait for this wave's loads of the step's chunk,
+  // barrier (every wave's loads of the step have landed and every wave is
+  // done with the stage about to be refilled), refill that stage, compute.
+  for (int k = 0; k < RG::R - 1 && gp + kGroups * k < nch; ++k) {
+    int pa, pb;
+    chunk_pages(pages_addr, gp + kGroups * k, pa, pb);
+    issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, r, lane);
+  }
+  for (int k = 0; k < nst; ++k) {
+    const int ck = gp + kGroups * k;
+    if (gp + kGroups * (k + RG::R - 2) < nch) {
+      if (FP8 && r == 0) wait_vm<RG::WAIT0>();
       else wait_vm<RG::WAIT>();
     } else {
       wait_vm<0>();
     }
     ring_barrier();
-    if (k + RG::R - 1 < nch)
-      issue_chunk<D, FP8>(A, sm, sm.ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, k + RG::R - 1,
-                          g, w, lane);
-    if (active)
-      compute_chunk<D, FP8>(S, sm.ring + (k % RG::R) * RG::STAGE, tokbase + k * kChunk, tv0, tv1,
+    const int cn = gp + kGroups * (k + RG::R - 1);
+    if (cn < nch) {
+      int pa, pb;
+      chunk_pages(pages_addr, cn, pa, pb);
+      issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, r, lane);
+    }
+    if (active && ck < nch)
+      compute_chunk<D, FP8>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1,
                             L, q, W, A.scale_log2, lane);
   }
-  if (!active) return;
+
+  // ---- Merge the groups: group 1's waves hand (m, l, O) of their tile to
+  // group 0's through LDS (the rings are free once every wave is past the
+  // barrier; every wave's loads have completed, its last wait was vmcnt(0)).
+  S.l = xlane_sum4(S.l);
+  __syncthreads();
+  f32x4* xo = reinterpret_cast<f32x4*>(&sm.ring[0][0]);       // [tile][mt][lane]
+  float* xm = reinterpret_cast<float*>(&sm.ring[0][0]) + kGroupWaves * C::MT * 64 * 4;  // [tile][lane][m, l]
+  if (gp == 1 && active) {
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) xo[(r * C::MT + mt) * 64 + lane] = S.o[mt];
+    xm[(r * 64 + lane) * 2] = S.m;
+    xm[(r * 64 + lane) * 2 + 1] = S.l;
+  }
+  __syncthreads();
+  if (gp == 1 || !active) return;
+  {
+    const float m1 = xm[(r * 64 + lane) * 2], l1 = xm[(r * 64 + lane) * 2 + 1];
+    const float M = fmaxf(S.m, m1);
+    const float a0 = (S.m == -INFINITY) ? 0.f : fast_exp2(S.m - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = S.o[mt] * a0 + xo[(r * C::MT + mt) * 64 + lane] * a1;
+    S.l = S.l * a0 + l1 * a1;
+    S.m = M;
+  }
 
   // ---- Epilogue: the wave writes its rows (lane: row n, d = 16 mt + 4 c + i).
-  S.l = xlane_sum4(S.l);
-  const int row = 16 * w + n;
+  const int row = 16 * r + n;
   if (row >= rows) return;
   const int i = row / G, hh = row % G;
   const int h = g * G + hh;
   if (it.slot < 0) {
-    float zs = -INFINITY;
-    if (A.sinks_mode == 1) zs = A.sinks[h] * kLog2e;
-    else if (A.sinks_mode == 2) zs = A.sinks[(int64_t)b * Hq + h] * kLog2e;
+    const float zs = sink_log2(A, b, h);
     const float Mx = fmaxf(S.m, zs);
     const float a = fast_exp2(S.m - Mx);
     const float den = S.l * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
-    const float r = a / den;
+    const float rs = a / den;
     const int64_t ob = ((int64_t)(it.q_off + i) * Hq + h) * D + 4 * c;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      const f32x4 v = S.o[mt] * r;
-      if (A.out_fp32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + ob + 16 * mt) = v;
-      } else {
-        bf16x2 p0 = {(__bf16)v[0], (__bf16)v[1]};
-        bf16x2 p1 = {(__bf16)v[2], (__bf16)v[3]};
-        uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-        *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + ob + 16 * mt) = pk;
-      }
-    }
+    for (int mt = 0; mt < C::MT; ++mt) store_out<D, FP8>(A, ob + 16 * mt, S.o[mt] * rs);
   } else {
     const int64_t pr = (int64_t)it.slot * A.rows_stride + row;
 #pragma unroll
@@ -614,29 +676,28 @@ __global__ __launch_bounds__(kThreads, 3) void pa_partition_kernel(KernelArgs A)
   }
 }
 
-// Log-sum-exp merge of the partials of one (sequence, KV head):
+// Log-sum-exp merge of the partials of one split (sequence, KV head):
 //   M = max(max_k m_k, z), Z = sum_k l_k 2^(m_k - M) + 2^(z - M),
 //   out = sum_k 2^(m_k - M) O_k / Z       (all in log2 units).
 // Grid: (reduce item, row, quarter of D); 256 threads = 8 column lanes (4
-// values each) x 32 partition lanes, so a row's partials are read 32 at a
-// time and no thread walks more than n_parts / 32 of them. The partition
-// lanes combine through LDS in a fixed order.
+// values each) x 32 partition lanes. Each thread folds its partials in one
+// pass with a running maximum; the partition lanes then combine through
+// LDS in a fixed order.
 constexpr int kRedCols = 8;
 constexpr int kRedParts = 256 / kRedCols;
 
 template <int D>
 __global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
   constexpr int DSPLIT = D / 4 / kRedCols;
-  __shared__ float s_m[kRedParts];
-  __shared__ float s_z[kRedParts];
+  __shared__ float s_m[kRedParts][kRedCols];
+  __shared__ float s_z[kRedParts][kRedCols];
   __shared__ f32x4 s_o[kRedParts][kRedCols];
   const int bid = blockIdx.x;
   const int ds = bid % DSPLIT;
-  const int row = (bid / DSPLIT) % kMaxRows;
-  const ReduceItem ri = A.red[bid / (DSPLIT * kMaxRows)];
-  const SeqInfo si = A.seqs[ri.seq];
+  const int row = (bid / DSPLIT) % A.rows_stride;
+  const ReduceItem ri = A.red[bid / (DSPLIT * A.rows_stride)];
   const int G = A.group, Hq = A.num_q_heads;
-  const int rows = si.q_len * G;
+  const int rows = ri.q_len * G;
   if (row >= rows) return;  // uniform over the workgroup
   const int dl = threadIdx.x % kRedCols, pl = threadIdx.x / kRedCols;
   const int d = (ds * kRedCols + dl) * 4;
@@ -646,56 +707,45 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
   const int64_t mstride = (int64_t)A.rows_stride * 2;
   const int64_t ostride = (int64_t)A.rows_stride * D;
 
-  float m = -INFINITY;
-#pragma unroll 4
-  for (int k = pl; k < n; k += kRedParts) m = fmaxf(m, ml[k * mstride]);
-  if (dl == 0) s_m[pl] = m;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int j = 0; j < kRedParts; ++j) M = fmaxf(M, s_m[j]);
-  float zs = -INFINITY;
-  const int i = row / G, hh = row % G;
-  const int h = ri.kv_head * G + hh;
-  if (A.sinks_mode == 1) zs = A.sinks[h] * kLog2e;
-  else if (A.sinks_mode == 2) zs = A.sinks[(int64_t)ri.seq * Hq + h] * kLog2e;
-  const float Mx = fmaxf(M, zs);
-
-  float z = 0.f;
+  float M = -INFINITY, z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int k = pl; k < n; k += kRedParts) {
     const float2 v = *reinterpret_cast<const float2*>(ml + k * mstride);
     const f32x4 o = *reinterpret_cast<const f32x4*>(po + k * ostride);
-    const float wk = (v.x == -INFINITY) ? 0.f : fast_exp2(v.x - Mx);
-    z += v.y * wk;
-    acc += o * wk;
+    if (v.x == -INFINITY) continue;  // no key of that item is visible to the row
+    const float Mn = fmaxf(M, v.x);
+    const float a = fast_exp2(M - Mn);  // 0 while M is -inf
+    const float wk = fast_exp2(v.x - Mn);
+    acc = acc * a + o * wk;
+    z = z * a + v.y * wk;
+    M = Mn;
   }
-  if (dl == 0) s_z[pl] = z;
+  s_m[pl][dl] = M;
+  s_z[pl][dl] = z;
   s_o[pl][dl] = acc;
   __syncthreads();
   if (pl != 0) return;
+  const int i = row / G, hh = row % G;
+  const int h = ri.kv_head * G + hh;
+  const float zs = sink_log2(A, ri.seq, h);
+  float Mx = zs;
+  for (int j = 0; j < kRedParts; ++j) Mx = fmaxf(Mx, s_m[j][dl]);
   float Z = (zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx);
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < kRedParts; ++j) {
-    Z += s_z[j];
-    tot += s_o[j][dl];
+    const float mj = s_m[j][dl];
+    const float wj = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mx);
+    Z += s_z[j][dl] * wj;
+    tot += s_o[j][dl] * wj;
   }
-  tot *= 1.0f / Z;
-  const int64_t oi = ((int64_t)(si.q_off + i) * Hq + h) * D + d;
-  if (A.out_fp32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(A.out) + oi) = tot;
-  } else {
-    bf16x2 p0 = {(__bf16)tot[0], (__bf16)tot[1]};
-    bf16x2 p1 = {(__bf16)tot[2], (__bf16)tot[3]};
-    uint2 pk = make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
-    *reinterpret_cast<uint2*>(static_cast<__bf16*>(A.out) + oi) = pk;
-  }
+  store_out<D, false>(A, ((int64_t)(ri.q_off + i) * Hq + h) * D + d, tot * (1.0f / Z));
 }
 
-hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8,
+hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
+  if (ntmax < 1 || ntmax > kGroupWaves) return hipErrorInvalidValue;
   dim3 grid(n_items), block(kThreads);
   if (head_dim == 128) {
     if (fp8) hipLaunchKernelGGL((pa_partition_kernel<128, true>), grid, block, 0, stream, a);
@@ -707,18 +757,14 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, hipStream_t stream) {
+hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
+                         hipStream_t stream) {
   if (n_red <= 0) return hipSuccess;
   dim3 block(256);
-  if (head_dim == 128) {
-    constexpr int split = 128 / 4 / kRedCols;
-    hipLaunchKernelGGL((pa_reduce_kernel<128>), dim3(n_red * kMaxRows * split), block, 0, stream,
-                       a);
-  } else {
-    constexpr int split = 64 / 4 / kRedCols;
-    hipLaunchKernelGGL((pa_reduce_kernel<64>), dim3(n_red * kMaxRows * split), block, 0, stream,
-                       a);
-  }
+  const int split = head_dim / 4 / kRedCols;
+  dim3 grid((unsigned)n_red * rows_stride * split);
+  if (head_dim == 128) hipLaunchKernelGGL((pa_reduce_kernel<128>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((pa_reduce_kernel<64>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

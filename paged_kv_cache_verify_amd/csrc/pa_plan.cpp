@@ -23,18 +23,34 @@
 
 using namespace pav;
 
+namespace {
+
+// Host-side record of one sequence while the plan is built.
+struct SeqInfo {
+  int32_t ctx_len;   // L
+  int32_t q_len;     // q (0: padded slot)
+  int32_t q_off;     // first query row of this sequence in q/out
+  int32_t lo;        // first key any row may see (window), else 0
+  int32_t window;    // W, 0 = none
+  int32_t n_parts;   // work items per KV head
+  int32_t piece;     // keys per work item (the last one may be shorter)
+  int32_t slot_base; // partial slot of (kv head 0, part 0) when n_parts > 1
+};
+
+}  // namespace
+
 struct pa_plan_s {
   int device = -1;
+  int cus = 0;  // compute units of the device the plan was built for
   pa_shape shape{};
   std::vector<SeqInfo> seqs;
   std::vector<WorkItem> items;
-  std::vector<ReduceItem> red;
   int64_t kv_bytes = 0;
   int64_t scratch_bytes = 0;
   int32_t partition_tokens = 0;
   int32_t rows_stride = 0;
   int64_t n_slots = 0;
-  SeqInfo* d_seqs = nullptr;
+  std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
   WorkItem* d_items = nullptr;
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
@@ -67,12 +83,10 @@ void release_device(pa_plan_s* p) {
   int cur = 0;
   bool have = hipGetDevice(&cur) == hipSuccess;
   if (have && cur != p->device) (void)hipSetDevice(p->device);
-  if (p->d_seqs) (void)hipFree(p->d_seqs);
   if (p->d_items) (void)hipFree(p->d_items);
   if (p->d_red) (void)hipFree(p->d_red);
   if (p->d_part_o) (void)hipFree(p->d_part_o);
   if (p->d_part_ml) (void)hipFree(p->d_part_ml);
-  p->d_seqs = nullptr;
   p->d_items = nullptr;
   p->d_red = nullptr;
   p->d_part_o = nullptr;
@@ -146,16 +160,42 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
   return PA_OK;
 }
 
-// Keys per work item when the caller leaves the choice to the plan: enough
-// items for about two rounds of one workgroup per CU, each large enough to
-// amortise its prologue and epilogue.
-int32_t auto_partition(int64_t total_keys) {
-  const int64_t target_items = 2 * 256;
-  int64_t p = (total_keys + target_items - 1) / target_items;
-  p = ((p + kChunk - 1) / kChunk) * kChunk;
-  p = std::max<int64_t>(p, 256);
-  p = std::min<int64_t>(p, kMaxItemKeys);
-  return (int32_t)p;
+// Work items of (at most) `piece` keys for every active sequence, counted
+// over all KV heads.
+int64_t count_items(const std::vector<SeqInfo>& seqs, int Hkv, int64_t piece) {
+  int64_t n = 0;
+  for (const SeqInfo& si : seqs) {
+    if (si.q_len == 0) continue;
+    const int64_t span = si.ctx_len - (si.lo / kBlock) * kBlock;
+    n += Hkv * ((span + piece - 1) / piece);
+  }
+  return n;
+}
+
+// Item size when the caller leaves the choice to the plan. One workgroup
+// runs per CU, so the plan looks for the smallest size (a multiple of 32
+// keys) whose items fit one round on the device; the workgroups then start
+// together and each streams about the same number of keys. When no size up
+// to the item limit fits one round, items of about a third of a round's
+// share keep the rounds' tails short.
+int64_t auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus) {
+  int64_t total = 0;
+  for (const SeqInfo& si : seqs)
+    if (si.q_len > 0) total += (int64_t)Hkv * (si.ctx_len - (si.lo / kBlock) * kBlock);
+  if (total == 0) return kChunk;
+  auto round32 = [](int64_t x) { return ((x + kChunk - 1) / kChunk) * kChunk; };
+  if (count_items(seqs, Hkv, kMaxItemKeys) <= cus) {
+    int64_t lo = std::max<int64_t>(kChunk, round32((total + cus - 1) / cus)), hi = kMaxItemKeys;
+    lo = std::min(lo, hi);
+    while (lo < hi) {  // smallest multiple of 32 in [lo, hi] that fits one round
+      const int64_t mid = round32((lo + hi) / 2);
+      if (mid >= hi) break;
+      if (count_items(seqs, Hkv, mid) <= cus) hi = mid;
+      else lo = mid + kChunk;
+    }
+    return hi;
+  }
+  return std::min<int64_t>(kMaxItemKeys, std::max<int64_t>(512, round32(total / (3LL * cus))));
 }
 
 }  // namespace
@@ -176,10 +216,20 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
   const int esz = s.kv_dtype == PA_FP8_E4M3 ? 1 : 2;
   const int64_t tok_bytes = 2LL * s.head_dim * esz + (s.kv_dtype == PA_FP8_E4M3 ? 8 : 0);
 
+  // Work items are sized for the device's CU count (256 on MI355X, assumed
+  // for a host-only plan).
+  int cus = 256;
+  if (device >= 0) {
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    if (cus < 1) cus = 1;
+  }
+
   pa_plan_s* p = new (std::nothrow) pa_plan_s();
   if (!p) return fail(PA_E_NOMEM, "host allocation of the plan failed");
   p->shape = s;
   p->device = device;
+  p->cus = cus;
 
   try {
     p->seqs.resize(B);
@@ -195,6 +245,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       if (si.q_len > 0 && si.window > 0)
         si.lo = std::max(0, si.ctx_len - si.q_len - si.window + 1);
       si.n_parts = 0;
+      si.piece = 0;
       si.slot_base = -1;
       q_off += si.q_len;
       if (si.q_len > 0) {
@@ -204,18 +255,31 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     }
     p->rows_stride = rows_stride;
     p->kv_bytes = total_keys * tok_bytes;
-    const int32_t P = s.partition_tokens > 0 ? s.partition_tokens : auto_partition(total_keys);
-    p->partition_tokens = P;
 
-    // Cut [lo, L) of every active sequence at multiples of P counted from
-    // lo rounded down to a page, the same cut for every KV head.
+    // Cut [a, L) of every active sequence, a = lo rounded down to a page,
+    // into pieces of one size per sequence (a multiple of 16 keys, so every
+    // cut falls on a page boundary), the same for every KV head. A caller's
+    // partition_tokens is that size for every sequence; otherwise each
+    // sequence is cut into as few equal pieces of at most the plan's item
+    // size as will do.
+    const int64_t limit = s.partition_tokens > 0 ? s.partition_tokens
+                                                 : auto_piece(p->seqs, Hkv, cus);
     int64_t slots = 0;
+    int32_t largest = 0;
     for (int b = 0; b < B; ++b) {
       SeqInfo& si = p->seqs[b];
       if (si.q_len == 0) continue;
       const int a = (si.lo / kBlock) * kBlock;
       const int span = si.ctx_len - a;
-      si.n_parts = (span + P - 1) / P;
+      si.n_parts = (int32_t)((span + limit - 1) / limit);
+      if (s.partition_tokens > 0) {
+        si.piece = (int32_t)limit;
+      } else {
+        const int per = (span + si.n_parts - 1) / si.n_parts;
+        si.piece = std::min<int32_t>((int32_t)limit, ((per + kBlock - 1) / kBlock) * kBlock);
+        si.n_parts = (span + si.piece - 1) / si.piece;
+      }
+      largest = std::max(largest, std::min(si.piece, span));
       if (si.n_parts > 1) {
         si.slot_base = (int32_t)slots;
         slots += (int64_t)Hkv * si.n_parts;
@@ -225,8 +289,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
           WorkItem it{};
           it.seq = b;
           it.kv_head = g;
-          it.key_begin = std::max(si.lo, a + k * P);
-          it.key_end = std::min(si.ctx_len, a + (k + 1) * P);
+          it.key_begin = std::max(si.lo, a + k * si.piece);
+          it.key_end = std::min(si.ctx_len, a + (k + 1) * si.piece);
           it.slot = si.n_parts > 1 ? (int32_t)(si.slot_base + (int64_t)g * si.n_parts + k) : -1;
           it.ctx_len = si.ctx_len;
           it.q_len = si.q_len;
@@ -235,25 +299,32 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
           p->items.push_back(it);
         }
         if (si.n_parts > 1) {
-          ReduceItem r{b, g, (int32_t)(si.slot_base + (int64_t)g * si.n_parts), si.n_parts};
+          ReduceItem r{};
+          r.seq = b;
+          r.kv_head = g;
+          r.slot_base = (int32_t)(si.slot_base + (int64_t)g * si.n_parts);
+          r.n_parts = si.n_parts;
+          r.q_len = si.q_len;
+          r.q_off = si.q_off;
           p->red.push_back(r);
         }
       }
     }
+    p->partition_tokens = s.partition_tokens > 0 ? s.partition_tokens : largest;
     for (const WorkItem& it : p->items) {
-      // A wave holds the page ids of its chunks in one register (64 lanes).
+      // A workgroup keeps the page ids of at most kMaxItemChunks chunks.
       const int span = it.key_end - (it.key_begin / kBlock) * kBlock;
-      if ((span + kChunk - 1) / kChunk > 64 * kWaves) {
+      if ((span + kChunk - 1) / kChunk > kMaxItemChunks) {
         delete p;
         return fail(PA_E_UNSUPPORTED, "a work item spans more than %d keys", kMaxItemKeys);
       }
     }
-    if (p->items.size() >= (size_t)INT32_MAX ||
-        p->red.size() * kMaxRows * 4 >= (size_t)INT32_MAX) {
+    if (p->items.size() >= (size_t)INT32_MAX || slots >= (int64_t)INT32_MAX ||
+        (int64_t)p->red.size() * rows_stride * 4 >= (int64_t)INT32_MAX) {
       delete p;
       return fail(PA_E_UNSUPPORTED, "the work list exceeds a 1-D grid");
     }
-    // Longest items first, so the short tails of split sequences fill in last.
+    // Longest items first, so the short ones fill in last.
     std::stable_sort(p->items.begin(), p->items.end(), [](const WorkItem& x, const WorkItem& y) {
       return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
     });
@@ -285,9 +356,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     if (r != hipSuccess) return r;
     return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
   };
-  e = upload((void**)&p->d_seqs, p->seqs.data(), p->seqs.size() * sizeof(SeqInfo));
-  if (e == hipSuccess)
-    e = upload((void**)&p->d_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+  e = upload((void**)&p->d_items, p->items.data(), p->items.size() * sizeof(WorkItem));
   if (e == hipSuccess)
     e = upload((void**)&p->d_red, p->red.data(), p->red.size() * sizeof(ReduceItem));
   if (e == hipSuccess && p->n_slots > 0) {
@@ -336,7 +405,6 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
   a.part_o = plan->d_part_o;
   a.part_ml = plan->d_part_ml;
   a.items = plan->d_items;
-  a.seqs = plan->d_seqs;
   a.red = plan->d_red;
   a.num_q_heads = s.num_q_heads;
   a.num_kv_heads = s.num_kv_heads;
@@ -351,11 +419,12 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
   hipError_t e;
   if (plan->ev_before && (e = hipEventRecord(plan->ev_before, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, st);
+  e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, (plan->rows_stride + 15) / 16,
+                       st);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_reduce(a, (int)plan->red.size(), s.head_dim, st);
+  e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   return PA_OK;
 }
