@@ -148,7 +148,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 
 constexpr int kGroups = 2;                 // token groups per workgroup
-constexpr int kGroupWaves = 4;             // waves per group (one per row tile)
+constexpr int kTileWaves = 4;              // compute waves per group (one per row tile)
+constexpr int kGroupWaves = kTileWaves + 1;  // ... and the group's loader
 constexpr int kWaves = kGroups * kGroupWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupRingBytes = 64 * 1024; // per group; the workgroup holds a CU's LDS
@@ -156,23 +157,26 @@ constexpr int kGroupRingBytes = 64 * 1024; // per group; the workgroup holds a C
 template <int D, bool FP8>
 struct Ring {
   using C = Cfg<D, FP8>;
+  using CB = Cfg<D, false>;                      // bf16 layout the compute reads
   static constexpr int KB = 2 * C::KLD * 1024;   // K of two pages, operand order
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  static constexpr int R0 = kGroupRingBytes / STAGE;
+  // FP8: the chunk the group computes on, converted to bf16 once (K in
+  // operand order, then the V tile in the bf16 swizzle).
+  static constexpr int KB16 = 2 * CB::KLD * 1024;
+  static constexpr int BUF = FP8 ? KB16 + CB::VLD * 1024 : 0;
+  static constexpr int R0 = (kGroupRingBytes - BUF) / STAGE;
   static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
-  static constexpr int T = 2 * C::KLD + C::VLD;  // 1 KiB loads per chunk
-  static constexpr int TW = T / kGroupWaves;     // ... issued by each wave of the group
-  static_assert(T % kGroupWaves == 0, "every wave issues the same number of loads");
+  // Loads per chunk, all issued by the group's loader wave: 1 KiB ones of
+  // K and V, and (FP8) one of the scales.
+  static constexpr int T = 2 * C::KLD + C::VLD + (FP8 ? 1 : 0);
   static_assert(R >= 3, "the ring needs at least three stages");
-  // Loads a wave may still have in flight when it starts on a chunk: those
-  // of its group's next R - 2 chunks (wave 0 of a group also loads the FP8
-  // scales).
-  static constexpr int WAIT = (R - 2) * TW;
-  static constexpr int WAIT0 = (R - 2) * (TW + (FP8 ? 1 : 0));
-  static_assert(WAIT0 <= 63, "vmcnt holds at most 63");
-  static constexpr int RING = R * STAGE;         // bytes per group
+  // Loads the loader may still have in flight when its group starts on a
+  // chunk: those of the group's next R - 2 chunks.
+  static constexpr int WAIT = (R - 2) * T;
+  static_assert(WAIT <= 63, "vmcnt holds at most 63");
+  static constexpr int RING = R * STAGE + BUF;   // bytes per group
 };
 
 template <int D, bool FP8>
@@ -226,34 +230,36 @@ __device__ __forceinline__ void chunk_pages(uint32_t pages_addr, int k, int& pa,
   pb = __builtin_amdgcn_readfirstlane(pp[1]);
 }
 
-// The wave's share of one chunk's loads into stage `sb` of its group's
-// ring. Wave r = 0 / 1 of the group loads K of the chunk's first / second
-// page (KLD loads of 1 KiB, in MFMA operand order: lane l of load u sits at
-// byte 1024 u + 16 l and is what lane l of the MFMA reads back); wave 2 / 3
-// loads V of the first / second page into the swizzled tile (lane l
-// fetches whichever source chunk belongs at its tile position). Wave 0 also
-// loads the FP8 scales. The lane's offsets are derived on every call (the
-// empty asm hides that they never change), rather than held in registers
-// across the loop.
+// All loads of one chunk into stage `sb` of the group's ring, issued by the
+// group's loader wave: K of the chunk's two pages (KLD loads of 1 KiB per
+// page, in MFMA operand order: lane l of load u sits at byte 1024 u + 16 l
+// and is what lane l of the MFMA reads back), V of the two pages into the
+// swizzled tile (lane l fetches whichever source chunk belongs at its tile
+// position), and the FP8 scales. The lane's offsets are derived on every
+// call (the empty asm hides that they never change), rather than held in
+// registers across the loop.
 template <int D, bool FP8>
 __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* sb, int pa,
-                                            int pb, int g, int r, int lane) {
+                                            int pb, int g, int lane) {
   using C = Cfg<D, FP8>;
   using RG = Ring<D, FP8>;
-  static_assert(RG::TW == C::KLD && 2 * RG::TW == C::VLD, "one page of K or V per wave");
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const int half = r & 1;
-  const int page = half ? pb : pa;
-  const int64_t base = ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
-  if (r < 2) {
-    const char* src = static_cast<const char*>(A.k_pool) + base;
-    const uint32_t off = (ln & 15) * C::ROWB + 16 * (ln >> 4);
+  const uint32_t koff = (ln & 15) * C::ROWB + 16 * (ln >> 4);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int page = half ? pb : pa;
+    const char* src = static_cast<const char*>(A.k_pool) +
+                      ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
     unsigned char* dst = sb + half * C::KLD * 1024;
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) dma16(src + (off + 64 * u), dst + u * 1024);
-  } else {
-    const char* src = static_cast<const char*>(A.v_pool) + base;
+    for (int u = 0; u < C::KLD; ++u) dma16(src + (koff + 64 * u), dst + u * 1024);
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int page = half ? pb : pa;
+    const char* src = static_cast<const char*>(A.v_pool) +
+                      ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
     unsigned char* dst = sb + RG::KB + half * (C::BLKB);
 #pragma unroll
     for (int u = 0; u < C::VLD / 2; ++u) {
@@ -264,14 +270,12 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
       dma16(src + (uint32_t)(tp * C::ROWB + ch * 16), dst + u * 1024);
     }
   }
-  if constexpr (FP8) {
-    if (r == 0) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
-      const int which = ln >> 4, tok = ln & 15;
-      const int pgs = (which & 1) ? pb : pa;
-      const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
-                          ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
-      dma4(src2, sb + RG::KB + RG::VB);
-    }
+  if constexpr (FP8) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
+    const int which = ln >> 4, tok = ln & 15;
+    const int pgs = (which & 1) ? pb : pa;
+    const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
+                        ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
+    dma4(src2, sb + RG::KB + RG::VB);
   }
 }
 
@@ -334,35 +338,6 @@ __device__ __forceinline__ void vt_reads_bf16_d64(s16x4 (&r)[8], const uint32_t 
       : "memory");
 }
 
-__device__ __forceinline__ void vt_reads_fp8_d128(i32x2 (&r)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %8\n\t"
-      "ds_read_b64_tr_b8 %1, %9\n\t"
-      "ds_read_b64_tr_b8 %2, %10\n\t"
-      "ds_read_b64_tr_b8 %3, %11\n\t"
-      "ds_read_b64_tr_b8 %4, %12\n\t"
-      "ds_read_b64_tr_b8 %5, %13\n\t"
-      "ds_read_b64_tr_b8 %6, %14\n\t"
-      "ds_read_b64_tr_b8 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-
-__device__ __forceinline__ void vt_reads_fp8_d64(i32x2 (&r)[4], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %4\n\t"
-      "ds_read_b64_tr_b8 %1, %5\n\t"
-      "ds_read_b64_tr_b8 %2, %6\n\t"
-      "ds_read_b64_tr_b8 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-      : "memory");
-}
-
 template <int D, bool FP8>
 struct WaveState {
   bf16x8 q[Cfg<D, FP8>::KS];
@@ -377,56 +352,46 @@ struct WaveState {
 // accumulators are not rescaled. O, l and m always share one reference.
 constexpr float kRescale = 8.0f;
 
-// One chunk for the wave's 16-row tile, from ring stage `sb`.
+// One chunk for the wave's 16-row tile. kv holds the chunk in the bf16
+// layout (K of the two pages in operand order, then the V tile); for FP8
+// it is the group's converted copy and scl the stage's K and V scales.
 template <int D, bool FP8>
-__device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsigned char* sb,
-                                              int tok0, int tv0, int tv1, int L, int q, int W,
-                                              float scale_log2, int lane) {
+__device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsigned char* kv,
+                                              const unsigned char* scl, int tok0, int tv0,
+                                              int tv1, int L, int q, int W, float scale_log2,
+                                              int lane) {
   using C = Cfg<D, FP8>;
+  using CB = Cfg<D, false>;
   using RG = Ring<D, FP8>;
   const int c = lane >> 4;
   const int i16 = lane & 15;
 
-  // ---- LDS reads of the stage: K operands, then every V^T operand (one
+  // ---- LDS reads of the chunk: K operands, then every V^T operand (one
   // asm block whose lgkmcnt(0) also covers the K reads), so both latencies
   // overlap.
-  u32x4 kr[2][C::KLD];
+  u32x4 kr[2][CB::KLD];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u)
-      kr[bb][u] = *reinterpret_cast<const u32x4*>(sb + (bb * C::KLD + u) * 1024 + lane * 16);
+    for (int u = 0; u < CB::KLD; ++u)
+      kr[bb][u] = *reinterpret_cast<const u32x4*>(kv + (bb * CB::KLD + u) * 1024 + lane * 16);
   f32x4 ksc[2], vs[2];
   if constexpr (FP8) {
-    const unsigned char* scl = sb + RG::KB + RG::VB;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       ksc[bb] = *reinterpret_cast<const f32x4*>(scl + (bb * 16 + 4 * c) * 4);
       vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
     }
   }
-  const uint32_t vt = lds_addr(sb + RG::KB);
+  const uint32_t vt = lds_addr(kv + RG::KB16);
   uint32_t va[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
-    if constexpr (FP8) {
-      const int r = i16 >> 1, k = i16 & 1;
-      const int t = 16 * (r >> 2) + 4 * c + (r & 3);
-      va[mt] = vt + vtile_chunk<D, FP8>(t, mt) + 8 * k;
-    } else {
-      const int r = i16 >> 2, k = i16 & 3;
-      va[mt] = vt + vtile_chunk<D, FP8>(4 * c + r, 2 * mt + (k >> 1)) + 8 * (k & 1);
-    }
+    const int r = i16 >> 2, k = i16 & 3;
+    va[mt] = vt + vtile_chunk<D, false>(4 * c + r, 2 * mt + (k >> 1)) + 8 * (k & 1);
   }
   bf16x8 vops[C::MT];
-  if constexpr (FP8) {
-    i32x2 codes[C::MT];
-    if constexpr (D == 128) vt_reads_fp8_d128(codes, va);
-    else vt_reads_fp8_d64(codes, va);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      vops[mt] = fp8x8_to_bf16((uint32_t)codes[mt][0], (uint32_t)codes[mt][1]);
-  } else {
+  {
     s16x4 rd[2 * C::MT];
     if constexpr (D == 128) vt_reads_bf16_d128(rd, va);
     else vt_reads_bf16_d64(rd, va);
@@ -436,20 +401,13 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
           bf16x8, __builtin_shufflevector(rd[2 * mt], rd[2 * mt + 1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // ---- S^T = K Q^T: the two pages' tokens on M, the tile's rows on N.
+// ---- S^T = K Q^T: the two pages' tokens on M, the tile's rows on N.
   f32x4 sc[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) {
-      if constexpr (FP8) {
-        acc = mfma_bf16(fp8x8_to_bf16(kr[bb][u][0], kr[bb][u][1]), S.q[2 * u], acc);
-        acc = mfma_bf16(fp8x8_to_bf16(kr[bb][u][2], kr[bb][u][3]), S.q[2 * u + 1], acc);
-      } else {
-        acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[bb][u]), S.q[u], acc);
-      }
-    }
+    for (int u = 0; u < CB::KLD; ++u) acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[bb][u]), S.q[u], acc);
     sc[bb] = FP8 ? acc * ksc[bb] : acc;
   }
 
@@ -460,6 +418,9 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
   const bool fast = (tok0 >= tv0) && (tok0 + kChunk <= tv1) && (tok0 + kChunk - 1 <= L - q) &&
                     (W == 0 || tok0 > L - 1 - W);
   if (!fast) {
+    // A real branch: the compiler would otherwise turn the selects into
+    // straight-line code that every chunk pays for.
+    asm volatile("");
     const int p = S.prow;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -482,6 +443,7 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
                    fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
   mx = xlane_max4(mx) * scale_log2;
   if (__any(mx > S.m + kRescale)) {
+    asm volatile("");  // a real branch (rescaling is rare)
     const float mnew = fmaxf(S.m, mx);
     const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
     S.m = mnew;
@@ -519,6 +481,49 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
   }
 }
 
+// FP8: the group's four waves convert the chunk in stage `st` to bf16 in
+// the group's buffer `buf`, exactly, each a quarter of it. K: wave r takes
+// 1 KiB block r of the stage (16 codes per lane = contraction steps 2u and
+// 2u + 1 of one token, which land in bf16 blocks 2u and 2u + 1). V: lane l
+// of wave r takes 16-byte chunk 64 r + l of the FP8 tile (16 columns of one
+// token), which lands as two bf16 chunks in the bf16 swizzle. LDS reads and
+// writes are issued from asm, so that the compiler does not hold them back
+// for the ring's in-flight loads.
+template <int D>
+__device__ __forceinline__ void convert_chunk(const unsigned char* st, unsigned char* buf, int r,
+                                              int lane) {
+  using C8 = Cfg<D, true>;
+  using CB = Cfg<D, false>;
+  using RG = Ring<D, true>;
+  constexpr int KBLK = 2 * C8::KLD;   // FP8 K blocks per chunk (4 for D 128, 2 for D 64)
+  constexpr int VCH = kChunk * D / 16; // FP8 V chunks of 16 bytes (256 / 128)
+  u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
+  const bool kdo = r < KBLK;
+  const int x = r * 64 + lane;
+  const bool vdo = x < VCH;
+  const int t = x / (D / 16), j = x % (D / 16);
+  const uint32_t ksrc = lds_addr(st + r * 1024 + lane * 16);
+  const uint32_t vsrc = lds_addr(st + RG::KB + t * C8::ROWB + ((j ^ vswz<D, true>(t)) << 4));
+  if (kdo) asm volatile("ds_read_b128 %0, %1" : "=v"(kw) : "v"(ksrc) : "memory");
+  if (vdo) asm volatile("ds_read_b128 %0, %1" : "=v"(vw) : "v"(vsrc) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kw), "+v"(vw) :: "memory");
+  if (kdo) {
+    const int bb = r / C8::KLD, u = r % C8::KLD;
+    const bf16x8 lo = fp8x8_to_bf16(kw[0], kw[1]), hi = fp8x8_to_bf16(kw[2], kw[3]);
+    const uint32_t d0 = lds_addr(buf + (bb * CB::KLD + 2 * u) * 1024 + lane * 16);
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024"
+                 :: "v"(d0), "v"(lo), "v"(hi) : "memory");
+  }
+  if (vdo) {
+    const bf16x8 lo = fp8x8_to_bf16(vw[0], vw[1]), hi = fp8x8_to_bf16(vw[2], vw[3]);
+    unsigned char* vb = buf + RG::KB16;
+    const uint32_t d0 = lds_addr(vb + vtile_chunk<D, false>(t, 2 * j));
+    const uint32_t d1 = lds_addr(vb + vtile_chunk<D, false>(t, 2 * j + 1));
+    asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3"
+                 :: "v"(d0), "v"(d1), "v"(lo), "v"(hi) : "memory");
+  }
+}
+
 template <int D, bool FP8>
 __device__ __forceinline__ void store_out(const KernelArgs& A, int64_t idx, f32x4 v) {
   if (A.out_fp32) {
@@ -547,12 +552,13 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int gp = w / kGroupWaves, r = w % kGroupWaves;     // token group, row tile
+  const bool loader = r == kTileWaves;                      // the group's loader
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
   const int L = it.ctx_len, q = it.q_len, W = it.window;
   const int rows = q * G;
-  const int nt = (rows + 15) >> 4;  // row tiles; waves r >= nt only load
+  const int nt = (rows + 15) >> 4;  // row tiles; waves r >= nt do not compute
   const bool active = r < nt;
   const int tv0 = it.key_begin, tv1 = it.key_end;
   const int tokbase = (tv0 >> 4) << 4;
@@ -598,33 +604,47 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
 
-  // Chunk of this wave's group at step k: gp + 2 k. Fill the first R - 1
-  // stages; then per step: wait for this wave's loads of the step's chunk,
-  // barrier (every wave's loads of the step have landed and every wave is
-  // done with the stage about to be refilled), refill that stage, compute.
-  for (int k = 0; k < RG::R - 1 && gp + kGroups * k < nch; ++k) {
-    int pa, pb;
-    chunk_pages(pages_addr, gp + kGroups * k, pa, pb);
-    issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, r, lane);
+  // Chunk of this wave's group at step k: gp + 2 k. The loader fills the
+  // first R - 1 stages; then per step: the loader waits for its loads of
+  // the step's chunk, the barrier (every group's chunk has landed and every
+  // wave is done with the stage about to be refilled), the loader refills
+  // that stage while the compute waves work. Compute waves never issue or
+  // wait for ring loads, so they never stall behind the load queue.
+  if (loader) {
+    for (int k = 0; k < RG::R - 1 && gp + kGroups * k < nch; ++k) {
+      int pa, pb;
+      chunk_pages(pages_addr, gp + kGroups * k, pa, pb);
+      issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, lane);
+    }
   }
   for (int k = 0; k < nst; ++k) {
     const int ck = gp + kGroups * k;
-    if (gp + kGroups * (k + RG::R - 2) < nch) {
-      if (FP8 && r == 0) wait_vm<RG::WAIT0>();
-      else wait_vm<RG::WAIT>();
-    } else {
-      wait_vm<0>();
+    if (loader) {
+      if (gp + kGroups * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
+      else wait_vm<0>();
     }
     ring_barrier();
     const int cn = gp + kGroups * (k + RG::R - 1);
-    if (cn < nch) {
+    if (loader && cn < nch) {
       int pa, pb;
       chunk_pages(pages_addr, cn, pa, pb);
-      issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, r, lane);
+      issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, lane);
     }
-    if (active && ck < nch)
-      compute_chunk<D, FP8>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1,
-                            L, q, W, A.scale_log2, lane);
+    const unsigned char* st = ring + (k % RG::R) * RG::STAGE;
+    if constexpr (FP8) {
+      // Convert the step's chunk once for the group, then a barrier makes
+      // the bf16 copy visible (every wave finished computing on the previous
+      // copy before the barrier above).
+      if (ck < nch) convert_chunk<D>(st, ring + RG::R * RG::STAGE, r, lane);
+      ring_barrier();
+      if (active && ck < nch)
+        compute_chunk<D, FP8>(S, ring + RG::R * RG::STAGE, st + RG::KB + RG::VB,
+                              tokbase + ck * kChunk, tv0, tv1, L, q, W, A.scale_log2, lane);
+    } else {
+      if (active && ck < nch)
+        compute_chunk<D, FP8>(S, st, nullptr, tokbase + ck * kChunk, tv0, tv1, L, q, W,
+                              A.scale_log2, lane);
+    }
   }
 
   // ---- Merge the groups: group 1's waves hand (m, l, O) of their tile to
