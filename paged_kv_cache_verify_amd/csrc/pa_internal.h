@@ -76,8 +76,9 @@ struct KernelArgs {
 // items with fewer rows skip the missing tiles. One workgroup per CU.
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             hipStream_t stream);
-// rows_stride: the most rows any reduce item has.
+// rows_stride: the most rows any reduce item has; max_parts: the most
+// partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
-                         hipStream_t stream);
+                         int max_parts, hipStream_t stream);
 
 }  // namespace pav

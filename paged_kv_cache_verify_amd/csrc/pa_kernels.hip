@@ -401,7 +401,7 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
           bf16x8, __builtin_shufflevector(rd[2 * mt], rd[2 * mt + 1], 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-// ---- S^T = K Q^T: the two pages' tokens on M, the tile's rows on N.
+  // ---- S^T = K Q^T: the two pages' tokens on M, the tile's rows on N.
   f32x4 sc[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
@@ -699,19 +699,18 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
 // Log-sum-exp merge of the partials of one split (sequence, KV head):
 //   M = max(max_k m_k, z), Z = sum_k l_k 2^(m_k - M) + 2^(z - M),
 //   out = sum_k 2^(m_k - M) O_k / Z       (all in log2 units).
-// Grid: (reduce item, row, quarter of D); 256 threads = 8 column lanes (4
-// values each) x 32 partition lanes. Each thread folds its partials in one
-// pass with a running maximum; the partition lanes then combine through
-// LDS in a fixed order.
-constexpr int kRedCols = 8;
-constexpr int kRedParts = 256 / kRedCols;
-
-template <int D>
-__global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
-  constexpr int DSPLIT = D / 4 / kRedCols;
-  __shared__ float s_m[kRedParts][kRedCols];
-  __shared__ float s_z[kRedParts][kRedCols];
-  __shared__ f32x4 s_o[kRedParts][kRedCols];
+// Grid: (reduce item, row, D / (4 COLS) column blocks); COLS x PARTS
+// threads = COLS column lanes (4 values each) x PARTS partition lanes. Each
+// thread folds its partials in one pass with a running maximum; the
+// partition lanes then combine through LDS in a fixed order. Two shapes:
+// few partials per pair (all columns of a row in one workgroup of 128
+// threads) and many (a quarter of the columns, 32 partition lanes).
+template <int D, int COLS, int PARTS>
+__global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
+  constexpr int DSPLIT = D / 4 / COLS;
+  __shared__ float s_m[PARTS][COLS];
+  __shared__ float s_z[PARTS][COLS];
+  __shared__ f32x4 s_o[PARTS][COLS];
   const int bid = blockIdx.x;
   const int ds = bid % DSPLIT;
   const int row = (bid / DSPLIT) % A.rows_stride;
@@ -719,27 +718,42 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
   const int G = A.group, Hq = A.num_q_heads;
   const int rows = ri.q_len * G;
   if (row >= rows) return;  // uniform over the workgroup
-  const int dl = threadIdx.x % kRedCols, pl = threadIdx.x / kRedCols;
-  const int d = (ds * kRedCols + dl) * 4;
+  const int dl = threadIdx.x % COLS, pl = threadIdx.x / COLS;
+  const int d = (ds * COLS + dl) * 4;
   const int n = ri.n_parts;
   const float* ml = A.part_ml + ((int64_t)ri.slot_base * A.rows_stride + row) * 2;
   const float* po = A.part_o + ((int64_t)ri.slot_base * A.rows_stride + row) * D + d;
   const int64_t mstride = (int64_t)A.rows_stride * 2;
   const int64_t ostride = (int64_t)A.rows_stride * D;
 
+  // Batches of U partials: all loads of a batch are in flight together,
+  // then they are folded in order.
+  constexpr int U = 4;
   float M = -INFINITY, z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = pl; k < n; k += kRedParts) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + k * mstride);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(po + k * ostride);
-    if (v.x == -INFINITY) continue;  // no key of that item is visible to the row
-    const float Mn = fmaxf(M, v.x);
-    const float a = fast_exp2(M - Mn);  // 0 while M is -inf
-    const float wk = fast_exp2(v.x - Mn);
-    acc = acc * a + o * wk;
-    z = z * a + v.y * wk;
-    M = Mn;
+  for (int k0 = pl; k0 < n; k0 += PARTS * U) {
+    float2 v[U];
+    f32x4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * PARTS;
+      v[u] = make_float2(-INFINITY, 0.f);
+      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < n) {
+        v[u] = *reinterpret_cast<const float2*>(ml + k * mstride);
+        o[u] = *reinterpret_cast<const f32x4*>(po + k * ostride);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // m = -inf: no key of that item is visible to the row (or no item).
+      const float Mn = fmaxf(M, v[u].x);
+      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+      const float wk = (v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - Mn);
+      acc = acc * a + o[u] * wk;
+      z = z * a + v[u].y * wk;
+      M = Mn;
+    }
   }
   s_m[pl][dl] = M;
   s_z[pl][dl] = z;
@@ -750,10 +764,12 @@ __global__ __launch_bounds__(256) void pa_reduce_kernel(KernelArgs A) {
   const int h = ri.kv_head * G + hh;
   const float zs = sink_log2(A, ri.seq, h);
   float Mx = zs;
-  for (int j = 0; j < kRedParts; ++j) Mx = fmaxf(Mx, s_m[j][dl]);
+#pragma unroll
+  for (int j = 0; j < PARTS; ++j) Mx = fmaxf(Mx, s_m[j][dl]);
   float Z = (zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx);
   f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < kRedParts; ++j) {
+#pragma unroll
+  for (int j = 0; j < PARTS; ++j) {
     const float mj = s_m[j][dl];
     const float wj = (mj == -INFINITY) ? 0.f : fast_exp2(mj - Mx);
     Z += s_z[j][dl] * wj;
@@ -778,13 +794,20 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
 }
 
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
-                         hipStream_t stream) {
+                         int max_parts, hipStream_t stream) {
   if (n_red <= 0) return hipSuccess;
-  dim3 block(256);
-  const int split = head_dim / 4 / kRedCols;
-  dim3 grid((unsigned)n_red * rows_stride * split);
-  if (head_dim == 128) hipLaunchKernelGGL((pa_reduce_kernel<128>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((pa_reduce_kernel<64>), grid, block, 0, stream, a);
+  const unsigned items = (unsigned)n_red * rows_stride;
+  if (max_parts <= 32) {  // one workgroup per row: 32 (D 128) or 16 column lanes x 4 or 8
+    if (head_dim == 128)
+      hipLaunchKernelGGL((pa_reduce_kernel<128, 32, 4>), dim3(items), dim3(128), 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_reduce_kernel<64, 16, 8>), dim3(items), dim3(128), 0, stream, a);
+  } else {  // 8 column lanes x 32 partition lanes per quarter (or half) of a row
+    if (head_dim == 128)
+      hipLaunchKernelGGL((pa_reduce_kernel<128, 8, 32>), dim3(items * 4), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_reduce_kernel<64, 8, 32>), dim3(items * 2), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct pa_plan_s {
   int32_t rows_stride = 0;
   int64_t n_slots = 0;
   std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
+  int32_t max_parts = 0;        // most partials of any split pair
   WorkItem* d_items = nullptr;
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
@@ -307,6 +308,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
           r.q_len = si.q_len;
           r.q_off = si.q_off;
           p->red.push_back(r);
+          p->max_parts = std::max(p->max_parts, si.n_parts);
         }
       }
     }
@@ -424,7 +426,7 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, st);
+  e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, plan->max_parts, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   return PA_OK;
 }
