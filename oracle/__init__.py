@@ -88,6 +88,10 @@ class Oracle:
         lib.pa_oracle_e4m3_to_double.restype = ctypes.c_double
         lib.pa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.pa_oracle_bf16_to_double.restype = ctypes.c_double
+        lib.pa_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.pa_oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.pa_oracle_kv_append.argtypes = [i32, i32, i32, P, P, P, P, P, i32, i32, i32, P, P, P, P]
+        lib.pa_oracle_kv_append.restype = i32
         self.lib = lib
 
     def e4m3_to_double(self, code: int) -> float:
@@ -130,6 +134,33 @@ class Oracle:
             raise ValueError(f"oracle rejected its arguments (code {rc})")
         return out, lse
 
+    def e4m3_encode(self, v: float) -> int:
+        """Nearest e4m3 code to fp32 value v (|v| <= 448), ties to even."""
+        return self.lib.pa_oracle_e4m3_encode(v)
+
+    def kv_append_arrays(self, *, num_kv_heads: int, head_dim: int, ctx_lens, q_lens,
+                         k_new_bits, v_new_bits, block_table, kv_fp8: bool, k_pool, v_pool,
+                         k_scales=None, v_scales=None):
+        """Paged KV append on host arrays, in place: the new rows (uint16 bf16
+        bits, [T][Hkv][D]) go into the pools (uint16 bf16 bits, or uint8 e4m3
+        codes with float32 scales). Pools and scales must be C-contiguous
+        numpy arrays; they are modified."""
+        ctx = _np(ctx_lens, np.int32)
+        ql = _np(q_lens, np.int32)
+        kn = _np(k_new_bits, np.uint16)
+        vn = _np(v_new_bits, np.uint16)
+        bt = _np(block_table, np.int32)
+        for a in (k_pool, v_pool) + ((k_scales, v_scales) if kv_fp8 else ()):
+            if not (isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"]):
+                raise ValueError("pools and scales must be C-contiguous numpy arrays")
+        rc = self.lib.pa_oracle_kv_append(
+            int(ctx.shape[0]), num_kv_heads, head_dim, _ptr(ctx), _ptr(ql), _ptr(kn), _ptr(vn),
+            _ptr(bt), int(bt.shape[1]), int(k_pool.shape[0]), int(kv_fp8), _ptr(k_pool),
+            _ptr(v_pool), _ptr(k_scales) if kv_fp8 else None,
+            _ptr(v_scales) if kv_fp8 else None)
+        if rc != 0:
+            raise ValueError(f"oracle rejected its arguments (code {rc})")
+
     def verify(self, wl, unit_mask=None, threads: Optional[int] = None):
         """Oracle output for a ``workloads.Workload`` whose tensors are on the CPU."""
         return self.verify_arrays(
@@ -161,3 +192,7 @@ def e4m3_to_double(code: int) -> float:
 
 def bf16_to_double(bits: int) -> float:
     return default().bf16_to_double(bits)
+
+
+def e4m3_encode(v: float) -> int:
+    return default().e4m3_encode(v)

@@ -259,3 +259,122 @@ int pa_oracle_verify(int B, int Hq, int Hkv, int D, const int32_t *ctx_lens,
   free(q_off);
   return rc;
 }
+
+/*
+ * Paged KV append with per-token FP8 quantisation: the step before verify
+ * attention, which writes the q new tokens' K and V into their 16-token
+ * slots through the block table.
+ *
+ * Sources: ATOM #3091 "High-interactivity monokernel decode for
+ * DeepSeek-V4.1-Flash on MI355X", Summary (stores into the paged pool are
+ * masked by row liveness: a padded slot, q = 0, stores nothing); ATOM #2843
+ * Motivation (FP8 KV with one fp32 scale per token and KV head); the FP8
+ * workload's scale rule, scale = amax / 448 of the token's values.
+ *
+ * For sequence b, new token i in [0, q) sits at position pos = L - q + i,
+ * page = bt[b][pos / 16], slot = pos % 16, and arrives as row t_b + i of the
+ * new K and V ([T][Hkv][D] bf16). For every KV head g:
+ *   bf16 pool: pool[page][g][slot][:] = the row, bit for bit;
+ *   FP8 pool:  x_d = the row's values (bf16, exact in fp32);
+ *              amax = max_d |x_d|; scale = amax / 448 in fp32 (1 if amax is 0);
+ *              code_d = the e4m3 value nearest to clamp(x_d / scale, -448, 448)
+ *                       (the division in fp32), ties to the even mantissa;
+ *              pool[page][g][slot][:] = the codes, scales[page][g][slot] = scale.
+ * Reading: the division and the scale are fp32 (the scales are fp32 and the
+ * FP8 workload quantises in fp32); amax = 0 gives scale 1 and zero codes.
+ */
+
+/* The e4m3 code nearest to v (|v| <= 448, not NaN), ties to the code with
+ * the even mantissa: a brute-force search over the 127 non-negative finite
+ * codes, decoded from the format definition above. The differences are exact
+ * in double (v has 24 significant bits, a code at most 4, both in
+ * [2^-9, 448]). */
+uint8_t pa_oracle_e4m3_encode(float v) {
+  const double a = fabs((double)v);
+  int best = 0;
+  double best_d = a; /* code 0 is +0 */
+  for (int c = 1; c <= 0x7E; ++c) {
+    const double d = fabs(a - pa_oracle_e4m3_to_double((uint8_t)c));
+    if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+static uint8_t *pool_row8(void *pool, int64_t page, int Hkv, int g, int slot, int D) {
+  return (uint8_t *)pool + ((page * Hkv + g) * PAGE_TOKENS + slot) * (int64_t)D;
+}
+static uint16_t *pool_row16(void *pool, int64_t page, int Hkv, int g, int slot, int D) {
+  return (uint16_t *)pool + ((page * Hkv + g) * PAGE_TOKENS + slot) * (int64_t)D;
+}
+
+/* Quantise one row of D bf16 values: codes and the fp32 scale. */
+static float quantise_row(const uint16_t *row, int D, uint8_t *codes) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    const float x = (float)pa_oracle_bf16_to_double(row[d]);
+    if (fabsf(x) > amax) amax = fabsf(x);
+  }
+  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int d = 0; d < D; ++d) {
+    const float x = (float)pa_oracle_bf16_to_double(row[d]);
+    float y = x / scale;
+    if (y > 448.0f) y = 448.0f;
+    if (y < -448.0f) y = -448.0f;
+    codes[d] = pa_oracle_e4m3_encode(y);
+  }
+  return scale;
+}
+
+/*
+ * Writes the new tokens into the pools as described above. Returns 0, or -1
+ * on arguments that cannot describe a valid call (nothing is written then).
+ * The caller's block table must give every new position a page < num_blocks.
+ */
+int pa_oracle_kv_append(int B, int Hkv, int D, const int32_t *ctx_lens, const int32_t *q_lens,
+                        const uint16_t *k_new, const uint16_t *v_new,
+                        const int32_t *block_table, int max_blocks, int num_blocks, int kv_fp8,
+                        void *k_pool, void *v_pool, float *k_scales, float *v_scales) {
+  if (B < 1 || Hkv < 1 || D < 1 || !ctx_lens || !q_lens || !k_new || !v_new || !block_table ||
+      !k_pool || !v_pool)
+    return -1;
+  if (kv_fp8 && (!k_scales || !v_scales)) return -1;
+  for (int b = 0; b < B; ++b) {
+    if (q_lens[b] < 0 || ctx_lens[b] < q_lens[b] ||
+        (int64_t)(ctx_lens[b] + PAGE_TOKENS - 1) / PAGE_TOKENS > max_blocks)
+      return -1;
+    for (int i = 0; i < q_lens[b]; ++i) {
+      const int pos = ctx_lens[b] - q_lens[b] + i;
+      const int32_t page = block_table[(int64_t)b * max_blocks + pos / PAGE_TOKENS];
+      if (page < 0 || page >= num_blocks) return -1;
+    }
+  }
+  uint8_t *codes = (uint8_t *)malloc((size_t)D);
+  if (!codes) return -1;
+  int64_t t = 0;
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i < q_lens[b]; ++i, ++t) {
+      const int pos = ctx_lens[b] - q_lens[b] + i;
+      const int64_t page = block_table[(int64_t)b * max_blocks + pos / PAGE_TOKENS];
+      const int slot = pos % PAGE_TOKENS;
+      for (int g = 0; g < Hkv; ++g) {
+        const uint16_t *kr = k_new + (t * Hkv + g) * (int64_t)D;
+        const uint16_t *vr = v_new + (t * Hkv + g) * (int64_t)D;
+        const int64_t si = (page * Hkv + g) * PAGE_TOKENS + slot;
+        if (kv_fp8) {
+          k_scales[si] = quantise_row(kr, D, codes);
+          memcpy(pool_row8(k_pool, page, Hkv, g, slot, D), codes, (size_t)D);
+          v_scales[si] = quantise_row(vr, D, codes);
+          memcpy(pool_row8(v_pool, page, Hkv, g, slot, D), codes, (size_t)D);
+        } else {
+          memcpy(pool_row16(k_pool, page, Hkv, g, slot, D), kr, (size_t)D * 2);
+          memcpy(pool_row16(v_pool, page, Hkv, g, slot, D), vr, (size_t)D * 2);
+        }
+      }
+    }
+  }
+  free(codes);
+  return 0;
+}

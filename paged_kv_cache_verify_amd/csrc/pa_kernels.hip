@@ -152,7 +152,10 @@ constexpr int kTileWaves = 4;              // compute waves per group (one per r
 constexpr int kGroupWaves = kTileWaves + 1;  // ... and the group's loader
 constexpr int kWaves = kGroups * kGroupWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGroupRingBytes = 64 * 1024; // per group; the workgroup holds a CU's LDS
+// LDS per group (the workgroup holds most of a CU's 160 KiB): 64 KiB for
+// bf16; 76 KiB for FP8, whose ring also holds two bf16 copies of chunks.
+template <bool FP8>
+constexpr int kGroupRingBytes = (FP8 ? 76 : 64) * 1024;
 
 template <int D, bool FP8>
 struct Ring {
@@ -162,20 +165,25 @@ struct Ring {
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  // FP8: the chunk the group computes on, converted to bf16 once (K in
-  // operand order, then the V tile in the bf16 swizzle).
+  // FP8: chunks converted to bf16 once per group (K in operand order, then
+  // the V tile in the bf16 swizzle), two copies: the one computed on and the
+  // one being converted for the next step.
   static constexpr int KB16 = 2 * CB::KLD * 1024;
-  static constexpr int BUF = FP8 ? KB16 + CB::VLD * 1024 : 0;
-  static constexpr int R0 = (kGroupRingBytes - BUF) / STAGE;
+  static constexpr int COPY = KB16 + CB::VLD * 1024;
+  static constexpr int BUF = FP8 ? 2 * COPY : 0;
+  static constexpr int R0 = (kGroupRingBytes<FP8> - BUF) / STAGE;
   static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
   // Loads per chunk, all issued by the group's loader wave: 1 KiB ones of
   // K and V, and (FP8) one of the scales.
   static constexpr int T = 2 * C::KLD + C::VLD + (FP8 ? 1 : 0);
-  static_assert(R >= 3, "the ring needs at least three stages");
+  static_assert(R >= (FP8 ? 4 : 3), "the ring needs enough stages to keep loads in flight");
   // Loads the loader may still have in flight when its group starts on a
-  // chunk: those of the group's next R - 2 chunks.
-  static constexpr int WAIT = (R - 2) * T;
-  static_assert(WAIT <= 63, "vmcnt holds at most 63");
+  // step: bf16 needs the step's chunk, so the next R - 2 chunks may be
+  // pending; FP8 converts one chunk ahead, so it needs the next chunk too
+  // and R - 3 may be pending. WAIT0: before the first FP8 conversion.
+  static constexpr int WAIT = (R - (FP8 ? 3 : 2)) * T;
+  static constexpr int WAIT0 = (R - 2) * T;
+  static_assert(WAIT0 <= 63, "vmcnt holds at most 63");
   static constexpr int RING = R * STAGE + BUF;   // bytes per group
 };
 
@@ -617,9 +625,22 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
       issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, lane);
     }
   }
+  unsigned char* cbuf = ring + RG::R * RG::STAGE;  // FP8: bf16 copies [2][COPY]
+  if constexpr (FP8) {
+    // The first chunk's copy, before the loop: wait for its stage (the next
+    // R - 2 stages may be pending), barrier, convert.
+    if (loader) {
+      if (gp + kGroups * (RG::R - 2) < nch) wait_vm<RG::WAIT0>();
+      else wait_vm<0>();
+    }
+    ring_barrier();
+    if (gp < nch) convert_chunk<D>(ring, cbuf, r, lane);
+  }
   for (int k = 0; k < nst; ++k) {
     const int ck = gp + kGroups * k;
     if (loader) {
+      // bf16: this step's chunk has landed; FP8: the next one too (it is
+      // converted during this step).
       if (gp + kGroups * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
       else wait_vm<0>();
     }
@@ -632,13 +653,14 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
     }
     const unsigned char* st = ring + (k % RG::R) * RG::STAGE;
     if constexpr (FP8) {
-      // Convert the step's chunk once for the group, then a barrier makes
-      // the bf16 copy visible (every wave finished computing on the previous
-      // copy before the barrier above).
-      if (ck < nch) convert_chunk<D>(st, ring + RG::R * RG::STAGE, r, lane);
-      ring_barrier();
+      // Convert the next chunk into the other copy (whose last reader, the
+      // previous step's compute, finished before the barrier above), then
+      // compute on this step's copy (converted during the previous step).
+      if (ck + kGroups < nch)
+        convert_chunk<D>(ring + ((k + 1) % RG::R) * RG::STAGE, cbuf + ((k + 1) & 1) * RG::COPY,
+                         r, lane);
       if (active && ck < nch)
-        compute_chunk<D, FP8>(S, ring + RG::R * RG::STAGE, st + RG::KB + RG::VB,
+        compute_chunk<D, FP8>(S, cbuf + (k & 1) * RG::COPY, st + RG::KB + RG::VB,
                               tokbase + ck * kChunk, tv0, tv1, L, q, W, A.scale_log2, lane);
     } else {
       if (active && ck < nch)

@@ -457,7 +457,177 @@ def pin_fp8_against_dequantised(orc):
         t += ql[b]
 
 
+# --------------------------------------------------------------------------
+# Pins: paged KV append and the e4m3 encoder.
+# --------------------------------------------------------------------------
+
+def _e4m3_values():
+    """The 127 non-negative finite e4m3 values, ascending (torch's decode)."""
+    codes = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_e4m3_encode_matches_torch(orc):
+    """The encoder against torch's float8_e4m3fn cast (round to nearest even)
+    on every finite value, every midpoint between neighbours (the ties),
+    points just off the midpoints, and random values over the whole range."""
+    vals = _e4m3_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    gen = torch.Generator().manual_seed(30)
+    rnd = (torch.rand(6000, generator=gen, dtype=torch.float64) * 2 - 1) * \
+        torch.exp2(torch.randint(-12, 9, (6000,), generator=gen).double())
+    pts = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+                          rnd.numpy()])
+    pts = pts.astype(np.float32)
+    pts = pts[np.abs(pts) <= 448.0]
+    pts = np.concatenate([pts, -pts, np.array([0.0, -0.0], dtype=np.float32)])
+    want = torch.from_numpy(pts).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(v)) for v in pts], dtype=np.uint8)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} codes differ, e.g. {pts[bad[:4]]}: {got[bad[:4]]} vs {want[bad[:4]]}"
+
+
+def pin_e4m3_encode_nearest(orc):
+    """Closed form: the decoded code is within half the local spacing of v,
+    and exact when v is representable."""
+    vals = _e4m3_values()
+    gen = torch.Generator().manual_seed(31)
+    v = ((torch.rand(3000, generator=gen, dtype=torch.float64) * 2 - 1) * 448).float().numpy()
+    for x in v:
+        c = orc.e4m3_encode(float(x))
+        dec = orc.e4m3_to_double(c)
+        a = abs(float(x))
+        k = int(np.searchsorted(vals, a))
+        lo = vals[max(k - 1, 0)]
+        hi = vals[min(k, len(vals) - 1)]
+        assert abs(abs(dec) - a) <= (hi - lo) / 2 + 1e-300, (x, dec)
+        assert (dec < 0) == (x < 0) or dec == 0
+    for c in range(0x7F):
+        assert orc.e4m3_encode(float(vals[c])) == c
+
+
+def _append_case(gen, fp8, D=32, Hkv=2):
+    ctx, ql = [37, 16, 64, 5, 90], [3, 0, 8, 5, 1]
+    B = len(ctx)
+    need = sum((L + 15) // 16 for L in ctx)
+    pool = 2 * need
+    perm = torch.randperm(pool, generator=gen)[:need]
+    bt = np.full((B, 8), pool - 1, dtype=np.int32)  # unused entries: an unreferenced page
+    o = 0
+    for b, L in enumerate(ctx):
+        n = (L + 15) // 16
+        bt[b, :n] = perm[o:o + n].numpy()
+        o += n
+    T = sum(ql)
+    kn = (torch.randn((T, Hkv, D), generator=gen) * 3).to(torch.bfloat16)
+    vn = (torch.randn((T, Hkv, D), generator=gen) * 3).to(torch.bfloat16)
+    if T:
+        kn[0, 0].zero_()  # a row with amax 0 (scale 1)
+    shape = (pool, Hkv, 16, D)
+    if fp8:
+        kp = np.full(shape, 0x7F, dtype=np.uint8)
+        vp = np.full(shape, 0x7F, dtype=np.uint8)
+        ks = np.full(shape[:3], np.nan, dtype=np.float32)
+        vs = np.full(shape[:3], np.nan, dtype=np.float32)
+    else:
+        kp = np.full(shape, 0x7FC0, dtype=np.uint16)
+        vp = np.full(shape, 0x7FC0, dtype=np.uint16)
+        ks = vs = None
+    return ctx, ql, bt, kn, vn, kp, vp, ks, vs
+
+
+def pin_kv_append_fp8(orc):
+    """FP8 append: every new (token, KV head) row lands at page bt[b][pos/16],
+    slot pos % 16, with the codes and scale of the workload quantiser (torch,
+    fp32); every other slot keeps its poison; q = 0 stores nothing."""
+    import workloads
+
+    gen = torch.Generator().manual_seed(32)
+    ctx, ql, bt, kn, vn, kp, vp, ks, vs = _append_case(gen, True)
+    kp0, vp0 = kp.copy(), vp.copy()
+    orc.kv_append_arrays(num_kv_heads=2, head_dim=32, ctx_lens=ctx, q_lens=ql,
+                         k_new_bits=bits(kn), v_new_bits=bits(vn), block_table=bt, kv_fp8=True,
+                         k_pool=kp, v_pool=vp, k_scales=ks, v_scales=vs)
+    kc, ksc = workloads.quantize_e4m3_per_token(kn.float())
+    vc, vsc = workloads.quantize_e4m3_per_token(vn.float())
+    written = np.zeros(kp.shape[:3], dtype=bool)
+    t = 0
+    for b, (L, q) in enumerate(zip(ctx, ql)):
+        for i in range(q):
+            pos = L - q + i
+            page, slot = bt[b, pos // 16], pos % 16
+            for g in range(2):
+                assert np.array_equal(kp[page, g, slot], kc[t, g].numpy()), (b, i, g)
+                assert np.array_equal(vp[page, g, slot], vc[t, g].numpy()), (b, i, g)
+                assert ks[page, g, slot] == ksc[t, g].item() and vs[page, g, slot] == vsc[t, g].item()
+                written[page, g, slot] = True
+            t += 1
+    assert np.array_equal(kp[~written], kp0[~written]) and np.array_equal(vp[~written], vp0[~written])
+    assert np.isnan(ks[~written]).all() and np.isnan(vs[~written]).all()
+    assert ks[written].min() > 0 and 1.0 in ks[written]  # the all-zero row keeps scale 1
+
+
+def pin_kv_append_bf16(orc):
+    """bf16 append copies the rows bit for bit into their slots, nothing else."""
+    gen = torch.Generator().manual_seed(33)
+    ctx, ql, bt, kn, vn, kp, vp, _, _ = _append_case(gen, False)
+    kp0 = kp.copy()
+    orc.kv_append_arrays(num_kv_heads=2, head_dim=32, ctx_lens=ctx, q_lens=ql,
+                         k_new_bits=bits(kn), v_new_bits=bits(vn), block_table=bt, kv_fp8=False,
+                         k_pool=kp, v_pool=vp)
+    written = np.zeros(kp.shape[:3], dtype=bool)
+    kb, vb = bits(kn), bits(vn)
+    t = 0
+    for b, (L, q) in enumerate(zip(ctx, ql)):
+        for i in range(q):
+            pos = L - q + i
+            page, slot = bt[b, pos // 16], pos % 16
+            assert np.array_equal(kp[page, :, slot], kb[t]) and np.array_equal(vp[page, :, slot], vb[t])
+            written[page, :, slot] = True
+            t += 1
+    assert np.array_equal(kp[~written], kp0[~written])
+
+
+def pin_append_then_attend(orc):
+    """Append, then attend: the new tokens written by the append oracle sit
+    where the attention oracle reads the last q keys, so attention over the
+    pool equals dense attention over the old context and the new rows."""
+    gen = torch.Generator().manual_seed(34)
+    Hq, Hkv, D = 4, 2, 16
+    ctx, ql = [40, 21], [4, 2]
+    qrows = rand_bf16(gen, (sum(ql), Hq, D))
+    dk = [rand_bf16(gen, (Hkv, L, D)) for L in ctx]
+    dv = [rand_bf16(gen, (Hkv, L, D)) for L in ctx]
+    kp, vp, bt = paged_from_dense(dk, dv, gen)
+    # poison the new tokens' slots, then write them back with the append
+    new_k = torch.cat([dk[b][:, ctx[b] - ql[b]:, :].transpose(0, 1) for b in range(2)])
+    new_v = torch.cat([dv[b][:, ctx[b] - ql[b]:, :].transpose(0, 1) for b in range(2)])
+    kpa, vpa = bits(kp).copy(), bits(vp).copy()
+    btn = bt.numpy()
+    for b in range(2):
+        for pos in range(ctx[b] - ql[b], ctx[b]):
+            kpa[btn[b, pos // 16], :, pos % 16] = 0x7FC0
+            vpa[btn[b, pos // 16], :, pos % 16] = 0x7FC0
+    orc.kv_append_arrays(num_kv_heads=Hkv, head_dim=D, ctx_lens=ctx, q_lens=ql,
+                         k_new_bits=bits(new_k.contiguous()), v_new_bits=bits(new_v.contiguous()),
+                         block_table=btn, kv_fp8=False, k_pool=kpa, v_pool=vpa)
+    sigma = 1.0 / math.sqrt(D)
+    out, _ = run(orc, Hq=Hq, Hkv=Hkv, D=D, ctx=ctx, ql=ql, q=qrows, kp=kpa, vp=vpa, bt=bt,
+                 sigma=sigma)
+    t = 0
+    for b in range(2):
+        ref = dense_attention(qrows[t:t + ql[b]].double(), dk[b].double(), dv[b].double(),
+                              ctx[b], ql[b], 0, sigma).numpy()
+        assert np.abs(out[t:t + ql[b]] - ref).max() < 1e-12
+        t += ql[b]
+
+
 ALL_PINS = [
+    pin_e4m3_encode_matches_torch,
+    pin_e4m3_encode_nearest,
+    pin_kv_append_fp8,
+    pin_kv_append_bf16,
+    pin_append_then_attend,
     pin_bruteforce_tiny,
     pin_bruteforce_config1,
     pin_paged_equals_dense,

@@ -53,6 +53,20 @@ MUTANTS = {
                  "const uint16_t *pool = (const uint16_t *)J->k_pool;"),
     # bf16 widened from the wrong half
     "bf16_low_half": ("uint32_t w = ((uint32_t)bits) << 16;", "uint32_t w = ((uint32_t)bits) << 15;"),
+    # append: new token written one slot later in its page
+    "append_slot": ("const int slot = pos % PAGE_TOKENS;", "const int slot = (pos + 1) % PAGE_TOKENS;"),
+    # append: the next block-table entry's page
+    "append_page": ("const int64_t page = block_table[(int64_t)b * max_blocks + pos / PAGE_TOKENS];",
+                    "const int64_t page = block_table[(int64_t)b * max_blocks + pos / PAGE_TOKENS + 1];"),
+    # quantiser: scale with the wrong divisor
+    "scale_divisor": ("amax / 448.0f", "amax / 447.0f"),
+    # encoder: ties to the odd mantissa
+    "ties_to_odd": ("(d == best_d && (c & 1) == 0 && (best & 1) == 1)",
+                    "(d == best_d && (c & 1) == 1 && (best & 1) == 0)"),
+    # encoder: sign dropped
+    "encode_no_sign": ("(signbit(v) ? 0x80 : 0)", "0"),
+    # append: V rows taken from the new K
+    "append_v_from_k": ("const uint16_t *vr = v_new + ", "const uint16_t *vr = k_new + "),
 }
 
 
