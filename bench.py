@@ -164,6 +164,53 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None):
     }
 
 
+def measure_append(wl, steps: int, warmup: int):
+    """Time pa_kv_append of the workload's new tokens (one call per step,
+    `steps` calls in one replayed HIP graph, host clock around the replay).
+    Returns the time per call and the call's algorithmic bytes: the bf16 K
+    and V rows read plus the pool rows (and FP8 scales) written."""
+    import torch
+
+    import paged_kv_cache_verify_amd as pav
+
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0)
+    T, Hkv, D = wl.total_q, wl.num_kv_heads, wl.head_dim
+    gen = torch.Generator().manual_seed(wl.seed + 1)
+    kn = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16).to("cuda:0")
+    vn = torch.randn((T, Hkv, D), generator=gen).to(torch.bfloat16).to("cuda:0")
+    fp8 = wl.kv_dtype == "fp8"
+    nbytes = 2 * T * Hkv * (2 * D + (D + 4 if fp8 else 2 * D))
+    s = torch.cuda.Stream()
+
+    def call():
+        pav.pa_kv_append(plan, kn, vn, dev.block_table, dev.k_pool, dev.v_pool, dev.k_scales,
+                         dev.v_scales, s)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(steps):
+            call()
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - w0) / steps
+    del g
+    pav.pa_free(plan)
+    return {"us_per_call": round(us, 2), "bytes_per_call": nbytes,
+            "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "new_tokens": T,
+            "timed_as": "hip-graph replay"}
+
+
 def cpu_baseline(wl, budget_s: float = 10.0):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -303,7 +350,16 @@ def main():
                 "work_items": rx["plan"]["work_items"],
                 "partition_tokens": rx["plan"]["partition_tokens"],
             }
+            if cfg in (3,) and P is None:
+                ra = measure_append(wlx, max(50, args.steps), max(5, args.warmup // 4))
+                log(f"  kv append of the {ra['new_tokens']} new tokens (FP8 quantise): "
+                    f"{ra['us_per_call']} us/call = {ra['GB_s']} GB/s")
+                extra[f"kv append, workload {cfg} shape (per-token FP8 quantise)"] = ra
             del wlx
+        ra = measure_append(wl, max(50, args.steps), max(5, args.warmup // 4))
+        log(f"kv append of workload {main_cfg}'s {ra['new_tokens']} new tokens (bf16): "
+            f"{ra['us_per_call']} us/call = {ra['GB_s']} GB/s")
+        extra[f"kv append, workload {main_cfg} shape (bf16 copy)"] = ra
         line["other_workloads"] = extra
 
     if not args.no_cpu_baseline and args.only is None:

@@ -144,6 +144,36 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q,
                            const float* v_scales, const float* sinks, void* out,
                            void* stream);
 
+/*
+ * Paged KV append: write the plan's new tokens (the last q_b positions of
+ * every sequence, L_b - q_b .. L_b - 1) into their 16-token slots, the step
+ * before verify attention. Source: ATOM #3091 ("High-interactivity
+ * monokernel decode for DeepSeek-V4.1-Flash on MI355X", Summary: stores into
+ * the paged pool are masked by row liveness, so a padded slot with q_b = 0
+ * stores nothing); ATOM #2843 (Motivation: FP8 KV with one fp32 scale per
+ * token and KV head, scale = amax / 448 of the token's values).
+ *   k_new, v_new  [T][Hkv][D] bf16, T = sum q_b, rows in sequence order (the
+ *                 layout of q with Hkv heads)
+ *   block_table   [B][max_blocks_per_seq] int32: position p of sequence b
+ *                 goes to page block_table[b][p / 16], slot p % 16
+ *   k_pool, v_pool [NB][Hkv][16][D] bf16 (copied bit for bit) or e4m3 codes
+ *   k_scales, v_scales [NB][Hkv][16] fp32, non-NULL exactly for FP8 KV: per
+ *                 (token, KV head) scale = amax / 448 in fp32 (1 when amax is
+ *                 0) and code = the e4m3 value nearest to the fp32 quotient
+ *                 x / scale clamped to +-448, ties to the even mantissa
+ * Only the new tokens' slots are written; a position whose block-table entry
+ * lies outside [0, num_blocks) is skipped, so no table can make the call
+ * store outside the pool. Enqueued on `stream` of the plan's device;
+ * asynchronous, allocation-free and graph-capturable like pa_decode_verify.
+ * Returns PA_E_INVALID for a missing pointer, scales given for bf16 KV or
+ * missing for FP8 KV, k_new/v_new/k_pool/v_pool not 4-byte aligned, or a
+ * host-only plan (nothing is launched then), PA_E_HIP if the launch fails.
+ * A plan whose sequences bring no new token returns PA_OK at once.
+ */
+pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,
+                       const int32_t* block_table, void* k_pool, void* v_pool,
+                       float* k_scales, float* v_scales, void* stream);
+
 /* Release a plan and its device memory. NULL-safe. The caller makes sure no
  * call that uses the plan is still in flight. */
 void pa_free(pa_plan_t* plan);

@@ -1,7 +1,7 @@
 """Paged verify attention for MI355X: a thin binding over libpa_verify.so.
 
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
-pa_free, pa_last_error, pa_plan_info, pa_plan_items,
+pa_kv_append, pa_free, pa_last_error, pa_plan_info, pa_plan_items,
 pa_set_partition_events). This module only marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
@@ -21,8 +21,8 @@ PA_OK, PA_E_INVALID, PA_E_UNSUPPORTED, PA_E_HIP, PA_E_NOMEM = 0, 1, 2, 3, 4
 PA_BF16, PA_FP8_E4M3, PA_FP32 = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
-EXPORTED = ("pa_plan", "pa_decode_verify", "pa_free", "pa_last_error", "pa_plan_info",
-            "pa_plan_items", "pa_set_partition_events")
+EXPORTED = ("pa_plan", "pa_decode_verify", "pa_kv_append", "pa_free", "pa_last_error",
+            "pa_plan_info", "pa_plan_items", "pa_set_partition_events")
 
 
 class PaShape(ctypes.Structure):
@@ -66,6 +66,8 @@ def library() -> ctypes.CDLL:
         lib.pa_plan.restype = ctypes.c_int
         lib.pa_decode_verify.argtypes = [P, P, P, P, P, P, P, P, P, P]
         lib.pa_decode_verify.restype = ctypes.c_int
+        lib.pa_kv_append.argtypes = [P, P, P, P, P, P, P, P, P]
+        lib.pa_kv_append.restype = ctypes.c_int
         lib.pa_free.argtypes = [P]
         lib.pa_free.restype = None
         lib.pa_last_error.argtypes = []
@@ -159,23 +161,36 @@ def _ptr(t) -> Optional[int]:
     if t is None:
         return None
     if not t.is_cuda:
-        raise ValueError("pa_decode_verify takes device tensors")
+        raise ValueError("the library takes device tensors")
     if not t.is_contiguous():
-        raise ValueError("pa_decode_verify takes contiguous tensors")
+        raise ValueError("the library takes contiguous tensors")
     return t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch  # torch provides the device memory and the stream
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
 def pa_decode_verify(plan: Plan, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
                      out, stream=None) -> None:
     """Enqueue one call on `stream` (default: torch's current stream)."""
-    import torch  # torch provides the device memory and the stream
-
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     _check(library().pa_decode_verify(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                       _ptr(block_table), _ptr(k_scales), _ptr(v_scales),
-                                      _ptr(sinks), _ptr(out), ctypes.c_void_p(handle)))
+                                      _ptr(sinks), _ptr(out), _stream_handle(stream)))
+
+
+def pa_kv_append(plan: Plan, k_new, v_new, block_table, k_pool, v_pool, k_scales=None,
+                 v_scales=None, stream=None) -> None:
+    """Store the plan's new tokens ([T][Hkv][D] bf16 K and V rows) into the
+    pools, quantising to e4m3 with per-token scales for FP8 KV (see
+    pa_kv_append in include/pa_verify.h). Enqueued on `stream`."""
+    _check(library().pa_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                                  _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
+                                  _stream_handle(stream)))
 
 
 def pa_free(plan: Plan) -> None:

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpa_verify.so")
-SOURCES = [os.path.join(CSRC, "pa_plan.cpp"), os.path.join(CSRC, "pa_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "pa_plan.cpp"), os.path.join(CSRC, "pa_kernels.hip"),
+           os.path.join(CSRC, "pa_append.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

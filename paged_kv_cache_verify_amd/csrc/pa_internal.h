@@ -72,6 +72,22 @@ struct KernelArgs {
   float scale_log2;  // softmax scale x log2(e)
 };
 
+// The new tokens of a verify step, for the paged KV append kernel.
+struct AppendArgs {
+  const uint16_t* k_new;       // [T][Hkv][D] bf16
+  const uint16_t* v_new;
+  const int32_t* block_table;  // [B][max_blocks]
+  const int32_t* tokens;       // [T][2]: sequence, position of new token t
+  void* k_pool;                // [num_blocks][Hkv][16][D] bf16 or e4m3
+  void* v_pool;
+  float* k_scales;             // [num_blocks][Hkv][16] (FP8 only)
+  float* v_scales;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t num_blocks;
+};
+
 // ntmax: row tiles of 16 the kernel is built for (ceil(max q x G / 16));
 // items with fewer rows skip the missing tiles. One workgroup per CU.
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
@@ -80,5 +96,6 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
 // partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
                          int max_parts, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int head_dim, bool fp8, hipStream_t stream);
 
 }  // namespace pav

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -52,7 +53,9 @@ struct pa_plan_s {
   int64_t n_slots = 0;
   std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
   int32_t max_parts = 0;        // most partials of any split pair
+  std::vector<int32_t> tokens;  // [T][2]: sequence, position of each new token
   WorkItem* d_items = nullptr;
+  int32_t* d_tokens = nullptr;
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
   float* d_part_ml = nullptr;
@@ -88,7 +91,9 @@ void release_device(pa_plan_s* p) {
   if (p->d_red) (void)hipFree(p->d_red);
   if (p->d_part_o) (void)hipFree(p->d_part_o);
   if (p->d_part_ml) (void)hipFree(p->d_part_ml);
+  if (p->d_tokens) (void)hipFree(p->d_tokens);
   p->d_items = nullptr;
+  p->d_tokens = nullptr;
   p->d_red = nullptr;
   p->d_part_o = nullptr;
   p->d_part_ml = nullptr;
@@ -249,6 +254,10 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       si.piece = 0;
       si.slot_base = -1;
       q_off += si.q_len;
+      for (int i = 0; i < si.q_len; ++i) {
+        p->tokens.push_back(b);
+        p->tokens.push_back(si.ctx_len - si.q_len + i);
+      }
       if (si.q_len > 0) {
         total_keys += (int64_t)Hkv * (si.ctx_len - si.lo);
         rows_stride = std::max(rows_stride, si.q_len * G);
@@ -361,6 +370,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
   e = upload((void**)&p->d_items, p->items.data(), p->items.size() * sizeof(WorkItem));
   if (e == hipSuccess)
     e = upload((void**)&p->d_red, p->red.data(), p->red.size() * sizeof(ReduceItem));
+  if (e == hipSuccess)
+    e = upload((void**)&p->d_tokens, p->tokens.data(), p->tokens.size() * sizeof(int32_t));
   if (e == hipSuccess && p->n_slots > 0) {
     e = hipMalloc((void**)&p->d_part_o,
                   (size_t)p->n_slots * p->rows_stride * s.head_dim * sizeof(float));
@@ -428,6 +439,41 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
     return hip_fail(e, "hipEventRecord");
   e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, plan->max_parts, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,
+                       const int32_t* block_table, void* k_pool, void* v_pool,
+                       float* k_scales, float* v_scales, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+  const pa_shape& s = plan->shape;
+  const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
+  if (plan->tokens.empty()) return PA_OK;  // no sequence brings a new token
+  if (!k_new || !v_new || !block_table || !k_pool || !v_pool)
+    return fail(PA_E_INVALID, "k_new, v_new, block_table, k_pool and v_pool are required");
+  if (fp8 && (!k_scales || !v_scales))
+    return fail(PA_E_INVALID, "FP8 KV needs k_scales and v_scales");
+  if (!fp8 && (k_scales || v_scales)) return fail(PA_E_INVALID, "bf16 KV takes no scales");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+       reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 3)
+    return fail(PA_E_INVALID, "k_new, v_new, k_pool and v_pool must be 4-byte aligned");
+
+  AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.block_table = block_table;
+  a.tokens = plan->d_tokens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.num_tokens = (int32_t)(plan->tokens.size() / 2);
+  a.num_kv_heads = s.num_kv_heads;
+  a.max_blocks = s.max_blocks_per_seq;
+  a.num_blocks = s.num_blocks;
+  hipError_t e = launch_append(a, s.head_dim, fp8, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
   return PA_OK;
 }
 

@@ -106,6 +106,8 @@ def test_null_arguments_are_refused():
     assert lib.pa_plan(ctypes.byref(shape), ctx, q, None, -1, None) == pav.PA_E_INVALID
     assert lib.pa_decode_verify(None, None, None, None, None, None, None, None, None,
                                 None) == pav.PA_E_INVALID
+    assert lib.pa_kv_append(None, None, None, None, None, None, None, None,
+                            None) == pav.PA_E_INVALID
     lib.pa_free(None)  # NULL-safe
 
 
@@ -116,6 +118,8 @@ def test_host_only_plan_refuses_to_run():
         st = pav.library().pa_decode_verify(plan.handle, 1, 1, 1, 1, None, None, None, 1, None)
         pav._check(st)
     assert e.value.status == pav.PA_E_INVALID
+    st = pav.library().pa_kv_append(plan.handle, 4, 4, 4, 4, 4, None, None, None)
+    assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
     plan.close()
 
 
