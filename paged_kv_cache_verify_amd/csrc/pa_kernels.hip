@@ -1,22 +1,23 @@
 // gfx950 kernels for paged verify attention.
 //
-// Partition kernel: one workgroup of eight waves per work item (and per
-// CU) = the keys [key_begin, key_end) of one (sequence, KV head), all q x G
-// packed rows of that KV head. The waves form two token groups of four:
+// Partition kernel: one workgroup of ten waves per work item (and per CU)
+// = the keys [key_begin, key_end) of one (sequence, KV head), all q x G
+// packed rows of that KV head. The waves form two token groups of five:
 // group 0 takes the item's even 32-token chunks (two 16-token pages), group
-// 1 the odd ones, each through an LDS ring of its own filled by direct
-// global-to-LDS loads that the group's four waves issue together (K in MFMA
-// A-operand order, V into an XOR-swizzled token-major tile); one workgroup
-// barrier per step recycles a stage in both rings. Within a group, wave r
-// owns row tile r (16 rows) and, per chunk,
+// 1 the odd ones, each through an LDS ring of its own that the group's
+// loader wave fills by direct global-to-LDS loads (K in MFMA A-operand
+// order, V into an XOR-swizzled token-major tile); one workgroup barrier per
+// step recycles a stage in both rings. Within a group, compute wave r owns
+// row tile r (16 rows) and, per chunk,
 //   1. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, tokens on the M
-//      index (FP8 codes are converted exactly to bf16 first and the
-//      per-token K scale multiplies the scores),
+//      index (FP8 codes are converted exactly to bf16 by the group's compute
+//      waves one step ahead, and the per-token K scale multiplies the
+//      scores),
 //   2. masks (causal within the query, window, key range) by selecting -inf,
 //   3. runs an online softmax in the exp2 domain whose reference max only
 //      moves when a chunk beats it by 2^8 (rare rescaling),
-//   4. accumulates O^T += V^T P^T: V^T comes from ds_read_b64_tr_b16 (or
-//      _tr_b8 for FP8) on the tile, P^T straight from the S^T accumulator
+//   4. accumulates O^T += V^T P^T: V^T comes from ds_read_b64_tr_b16 on
+//      the (bf16 or converted) tile, P^T straight from the S^T accumulator
 //      registers as a bf16 hi+lo pair (the per-token V scale folded in).
 // At the end the two groups' states of each tile merge through LDS and the
 // workgroup writes the output, or this item's partial, which the reduce
