@@ -10,6 +10,7 @@ namespace pav {
 constexpr int kBlock = 16;      // tokens per KV block
 constexpr int kChunk = 32;      // tokens a wave consumes per iteration (two blocks)
 constexpr int kMaxRows = 64;    // q x G packed rows per KV head (4 MFMA row tiles)
+constexpr int kMaxRows256 = 48; // ... at head_dim 256 (3 row tiles)
 constexpr int kMaxQuery = 8;
 constexpr int kMaxContext = 1 << 20;
 // Keys a work item spans from its page-aligned start; the workgroup keeps

@@ -40,28 +40,43 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <int D, bool FP8>
 struct Cfg {
-  static constexpr int KS = D / 32;                 // QK contraction steps of 32
+  static constexpr int KS = D / 32;                 // bf16 QK contraction steps of 32
+  static constexpr int KS8 = D >= 128 ? D / 128 : 1;  // FP8 QK steps of 128 (D 64: half used)
   static constexpr int MT = D / 16;                 // PV output tiles along D
   static constexpr int ESZ = FP8 ? 1 : 2;           // bytes per KV element
   static constexpr int ROWB = D * ESZ;              // bytes per token in a page
   static constexpr int BLKB = kBlock * ROWB;        // bytes per (page, KV head)
-  static constexpr int KLD = FP8 ? KS / 2 : KS;     // 16-byte K loads per page per lane
-  static constexpr int VLD = (2 * BLKB) / 1024;     // 16-byte V loads per chunk per lane
-  static_assert(BLKB >= 1024, "a 1 KiB V slab must stay inside one page");
-  static_assert(FP8 ? (KS % 2 == 0) : true, "FP8 loads cover two contraction steps");
+  static constexpr int KLD = BLKB / 1024;           // 1 KiB K loads per page
+  static constexpr int VLD = (2 * BLKB) / 1024;     // 1 KiB V loads per chunk
+  static_assert(BLKB >= 1024, "a 1 KiB slab must stay inside one page");
 };
 
-// Element offset of the 8 contraction values a lane holds for QK step s.
-// bf16: lane group c holds d = 32 s + 8 c .. +8 (64 contiguous bytes per
-// token across the 4 lane groups). FP8: one 16-byte load covers steps
-// 2u and 2u+1, d = 64 u + 16 c + 8 (s & 1) .. +8. Q uses the same map, so the
-// contraction order is a permutation of d that both operands share.
-template <int D, bool FP8>
-__device__ __forceinline__ int qk_dmap(int s, int c) {
-  return FP8 ? 64 * (s >> 1) + 16 * c + 8 * (s & 1) : 32 * s + 8 * c;
+// Compute waves per token group (one per 16-row tile): four, so up to 64
+// packed rows; three at D 256, whose waves need more registers (up to 48
+// rows).
+template <int D>
+constexpr int kTileWaves = D == 256 ? 3 : 4;
+
+// bf16 QK: lane group c holds d = 32 s + 8 c .. +8 of contraction step s
+// (64 contiguous bytes per token across the 4 lane groups); Q uses the same
+// map.
+__device__ __forceinline__ int qk_dmap(int s, int c) { return 32 * s + 8 * c; }
+
+// FP8 QK runs on v_mfma_f32_16x16x128_f8f6f4 with the codes as they are:
+// lane l holds 32 codes of token (or query row) l % 16 at d = 128 ks +
+// 32 (l / 16) + j, j = 0..31, for both operands (at D 64 lane groups 2 and 3
+// hold zeros). In the ring, K load u of a page puts the 16 bytes of token
+// l % 16 at d = 128 (u / 2) + 32 (l / 16) + 16 (u % 2) at byte 1024 u + 16 l
+// (D 64: one load, d = 16 (l / 16)).
+template <int D>
+__device__ __forceinline__ int k8_src(int u, int c) {
+  return D >= 128 ? 128 * (u >> 1) + 32 * c + 16 * (u & 1) : 16 * c;
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 acc) {
@@ -79,6 +94,16 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
   return r;
+}
+
+// The same eight codes -> eight fp16 values, exactly (e4m3's range and
+// precision fit inside fp16's).
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Reductions over the four lanes l, l^16, l^32, l^48 (the MFMA's four lane
@@ -121,7 +146,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <int D, bool FP8>
 __device__ __forceinline__ int vswz(int t) {
   if constexpr (FP8) {
-    return D == 128 ? ((t & 3) | (((t >> 4) & 1) << 2)) : (((t & 3) >> 1) | (((t >> 4) & 1) << 1));
+    if constexpr (D == 64) return ((t & 3) >> 1) | (((t >> 4) & 1) << 1);
+    else if constexpr (D == 128) return (t & 3) | (((t >> 4) & 1) << 2);
+    else return (t & 3) | (((t >> 4) & 1) << 2) | (((t >> 2) & 1) << 3);
   } else {
     return D == 128 ? (2 * (t & 3) + 8 * ((t >> 2) & 1)) : 2 * (t & 3);
   }
@@ -148,49 +175,40 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // The LDS rings: one per token group.
 // ---------------------------------------------------------------------------
 
-constexpr int kGroups = 2;                 // token groups per workgroup
-constexpr int kTileWaves = 4;              // compute waves per group (one per row tile)
-constexpr int kGroupWaves = kTileWaves + 1;  // ... and the group's loader
-constexpr int kWaves = kGroups * kGroupWaves;
-constexpr int kThreads = 64 * kWaves;
-// LDS per group (the workgroup holds most of a CU's 160 KiB): 64 KiB for
-// bf16; 76 KiB for FP8, whose ring also holds two bf16 copies of chunks.
-template <bool FP8>
-constexpr int kGroupRingBytes = (FP8 ? 76 : 64) * 1024;
+constexpr int kGroups = 2;  // token groups per workgroup
+template <int D>
+constexpr int kGroupWaves = kTileWaves<D> + 1;  // a group's compute waves and its loader
+template <int D>
+constexpr int kThreads = 64 * kGroups * kGroupWaves<D>;
+// LDS per group: the workgroup holds most of a CU's 160 KiB.
+constexpr int kGroupRingBytes = 76 * 1024;
 
 template <int D, bool FP8>
 struct Ring {
   using C = Cfg<D, FP8>;
-  using CB = Cfg<D, false>;                      // bf16 layout the compute reads
   static constexpr int KB = 2 * C::KLD * 1024;   // K of two pages, operand order
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  // FP8: chunks converted to bf16 once per group (K in operand order, then
-  // the V tile in the bf16 swizzle), two copies: the one computed on and the
-  // one being converted for the next step.
-  static constexpr int KB16 = 2 * CB::KLD * 1024;
-  static constexpr int COPY = KB16 + CB::VLD * 1024;
-  static constexpr int BUF = FP8 ? 2 * COPY : 0;
-  static constexpr int R0 = (kGroupRingBytes<FP8> - BUF) / STAGE;
+  static constexpr int R0 = kGroupRingBytes / STAGE;
   static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
   // Loads per chunk, all issued by the group's loader wave: 1 KiB ones of
   // K and V, and (FP8) one of the scales.
   static constexpr int T = 2 * C::KLD + C::VLD + (FP8 ? 1 : 0);
-  static_assert(R >= (FP8 ? 4 : 3), "the ring needs enough stages to keep loads in flight");
+  static_assert(R >= 3, "the ring needs enough stages to keep loads in flight");
   // Loads the loader may still have in flight when its group starts on a
-  // step: bf16 needs the step's chunk, so the next R - 2 chunks may be
-  // pending; FP8 converts one chunk ahead, so it needs the next chunk too
-  // and R - 3 may be pending. WAIT0: before the first FP8 conversion.
-  static constexpr int WAIT = (R - (FP8 ? 3 : 2)) * T;
-  static constexpr int WAIT0 = (R - 2) * T;
-  static_assert(WAIT0 <= 63, "vmcnt holds at most 63");
-  static constexpr int RING = R * STAGE + BUF;   // bytes per group
+  // step: the step's chunk must have landed, the next R - 2 may be pending.
+  static constexpr int WAIT = (R - 2) * T;
+  static_assert(WAIT <= 63, "vmcnt holds at most 63");
+  static constexpr int RING = R * STAGE;         // bytes per group
+  static_assert(STAGE % 256 == 0 && KB % 256 == 0, "stage addresses keep their low 8 bits zero");
 };
 
+// The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
+// FP8 V reads rely on the low 8 bits of a stage's address being zero.
 template <int D, bool FP8>
 struct Smem {
-  unsigned char ring[kGroups][Ring<D, FP8>::RING];
+  alignas(1024) unsigned char ring[kGroups][Ring<D, FP8>::RING];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
@@ -254,7 +272,7 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
   using RG = Ring<D, FP8>;
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const uint32_t koff = (ln & 15) * C::ROWB + 16 * (ln >> 4);
+  const uint32_t koff = (ln & 15) * C::ROWB + (FP8 ? k8_src<D>(0, ln >> 4) : 16 * (ln >> 4));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int page = half ? pb : pa;
@@ -262,7 +280,11 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
                       ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
     unsigned char* dst = sb + half * C::KLD * 1024;
 #pragma unroll
-    for (int u = 0; u < C::KLD; ++u) dma16(src + (koff + 64 * u), dst + u * 1024);
+    for (int u = 0; u < C::KLD; ++u) {
+      // bf16: load u covers d = 32 u + 8 (l / 16) .. +8 (contraction step u).
+      const uint32_t du = FP8 ? (D >= 128 ? 128 * (u >> 1) + 16 * (u & 1) : 0) : 64 * u;
+      dma16(src + (koff + du), dst + u * 1024);
+    }
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -347,9 +369,22 @@ __device__ __forceinline__ void vt_reads_bf16_d64(s16x4 (&r)[8], const uint32_t 
       : "memory");
 }
 
+// Query operands of the lane's row: bf16 (the bf16 MFMA's B operand), or for
+// FP8 KV two e4m3 terms, Q = qs (hi + lo), in the FP8 MFMA's B layout.
+template <int D, bool FP8>
+struct QOps {
+  bf16x8 q[Cfg<D, FP8>::KS];
+};
+template <int D>
+struct QOps<D, true> {
+  i32x8 hi[Cfg<D, true>::KS8];
+  i32x8 lo[Cfg<D, true>::KS8];
+  float qs;  // the row's power-of-two scale
+};
+
 template <int D, bool FP8>
 struct WaveState {
-  bf16x8 q[Cfg<D, FP8>::KS];
+  QOps<D, FP8> Q;
   f32x4 o[Cfg<D, FP8>::MT];
   float m;   // reference max of the lane's row (log2 units); p <= 2^kRescale
   float l;   // this lane's share of the row sum
@@ -361,38 +396,135 @@ struct WaveState {
 // accumulators are not rescaled. O, l and m always share one reference.
 constexpr float kRescale = 8.0f;
 
-// One chunk for the wave's 16-row tile. kv holds the chunk in the bf16
-// layout (K of the two pages in operand order, then the V tile); for FP8
-// it is the group's converted copy and scl the stage's K and V scales.
+// True when every key of the chunk lies in the item's range and is visible
+// to every row of the item (no masks needed).
+__device__ __forceinline__ bool chunk_interior(int tok0, int tv0, int tv1, int L, int q, int W) {
+  return (tok0 >= tv0) && (tok0 + kChunk <= tv1) && (tok0 + kChunk - 1 <= L - q) &&
+         (W == 0 || tok0 > L - 1 - W);
+}
+
+// Token of score element (bb, i) in lane group c: tok0 + 16 bb + 4 c + i.
+// Scores of keys the lane's row may not see become -inf (a select: the
+// pool slots of tokens outside the item's range may hold anything, NaN
+// included).
 template <int D, bool FP8>
-__device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsigned char* kv,
-                                              const unsigned char* scl, int tok0, int tv0,
-                                              int tv1, int L, int q, int W, float scale_log2,
-                                              int lane) {
+__device__ __forceinline__ void mask_scores(const WaveState<D, FP8>& S, f32x4 (&sc)[2], int tok0,
+                                            int tv0, int tv1, int W, int c) {
+  const int p = S.prow;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = tok0 + 16 * bb + 4 * c + i;
+      const bool vis = (j >= tv0) && (j < tv1) && (j <= p) && (W == 0 || j > p - W);
+      sc[bb][i] = vis ? sc[bb][i] : -INFINITY;
+    }
+  }
+}
+
+// Online softmax over one chunk in the exp2 domain (x = s * sigma * log2 e).
+// The state (m, l, O) keeps l = sum 2^(x - m) and O = sum 2^(x - m) V over
+// the keys so far, for a reference m that moves only when a chunk's largest x
+// exceeds m + kShift + kRescale (then m = that x - kShift, and O and l are
+// rescaled), so probabilities stay below 2^(kShift + kRescale). FP8 KV keeps
+// kShift = 6: its P enters an fp16 product, and the shift keeps small
+// probabilities clear of fp16's subnormal range. Adds the chunk's
+// probabilities to l and returns p w per score element, w the token's V scale
+// (FP8) or 1.
+template <int D, bool FP8>
+__device__ __forceinline__ void softmax_p(WaveState<D, FP8>& S, const f32x4 (&sc)[2],
+                                          const f32x4 (&vs)[2], float scale_log2, float (&pw)[8]) {
   using C = Cfg<D, FP8>;
-  using CB = Cfg<D, false>;
-  using RG = Ring<D, FP8>;
+  constexpr float kShift = FP8 ? 6.0f : 0.0f;
+  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  mx = xlane_max4(mx) * scale_log2;
+  if (__any(mx > S.m + (kShift + kRescale))) {
+    asm volatile("");  // a real branch (rescaling is rare)
+    const float mnew = fmaxf(S.m, mx - kShift);
+    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
+    S.m = mnew;
+    S.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] *= alpha;
+  }
+  const float msafe = (S.m == -INFINITY) ? 0.f : S.m;
+  float ps = 0.f;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(sc[bb][i], scale_log2, -msafe));
+      ps += p;
+      pw[4 * bb + i] = FP8 ? p * vs[bb][i] : p;
+    }
+  }
+  S.l += ps;
+}
+
+// P^T as two bf16 terms, hi = bf16(p w) and lo = bf16(p w - hi): its
+// rounding error (about 2^-17 relative) stays far below the output's own
+// bf16 rounding even when one key dominates a row.
+__device__ __forceinline__ void split_bf16(const float (&pw)[8], bf16x8& p_hi, bf16x8& p_lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 hi = (__bf16)pw[e];
+    p_hi[e] = hi;
+    p_lo[e] = (__bf16)(pw[e] - (float)hi);
+  }
+}
+
+// O^T[d][row] += V^T[d][token] P^T[token][row] for output tile mt. The
+// contraction index (lane group c, element e) is token 16 (e / 4) + 4 c +
+// e % 4 for both operands: that is where the S^T accumulator left P.
+__device__ __forceinline__ f32x4 pv_tile(bf16x8 v, bf16x8 p_hi, bf16x8 p_lo, f32x4 o) {
+  o = mfma_bf16(v, p_hi, o);
+  return mfma_bf16(v, p_lo, o);
+}
+
+// e4m3 (bias 7, largest finite 448) nearest to y, |y| <= 448, ties to the
+// even code, as an fp32 value: below 2^-6 the e4m3 values are the multiples
+// of 2^-9 (scaling by 2^9 is exact, rint rounds to even); above, fp32's 23
+// mantissa bits are rounded to 3 (a carry moves into the exponent).
+// (Both candidates are computed and one is selected: straight-line code.)
+__device__ __forceinline__ float e4m3_round(float y) {
+  const float a = fabsf(y);
+  const float sub = __builtin_rintf(a * 512.0f) * (1.0f / 512.0f);
+  const uint32_t b = __float_as_uint(a);
+  const float nrm = __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u);
+  return __builtin_copysignf(a < 0.015625f ? sub : nrm, y);
+}
+
+// The e4m3 code of an fp32 value that is exactly an e4m3 value.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  const uint32_t sub = (uint32_t)(a * 512.0f);
+  const uint32_t nrm = (__float_as_uint(a) >> 20) - (120u << 3);
+  return sign | (a < 0.015625f ? sub : nrm);
+}
+
+// One chunk for the wave's 16-row tile, bf16 KV: kv is the ring stage (K of
+// the two pages in operand order, then the V tile).
+template <int D>
+__device__ __forceinline__ void compute_chunk(WaveState<D, false>& S, const unsigned char* kv,
+                                              int tok0, int tv0, int tv1, int L, int q, int W,
+                                              float scale_log2, int lane) {
+  using C = Cfg<D, false>;
+  using RG = Ring<D, false>;
   const int c = lane >> 4;
   const int i16 = lane & 15;
 
   // ---- LDS reads of the chunk: K operands, then every V^T operand (one
   // asm block whose lgkmcnt(0) also covers the K reads), so both latencies
   // overlap.
-  u32x4 kr[2][CB::KLD];
+  u32x4 kr[2][C::KLD];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-    for (int u = 0; u < CB::KLD; ++u)
-      kr[bb][u] = *reinterpret_cast<const u32x4*>(kv + (bb * CB::KLD + u) * 1024 + lane * 16);
-  f32x4 ksc[2], vs[2];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      ksc[bb] = *reinterpret_cast<const f32x4*>(scl + (bb * 16 + 4 * c) * 4);
-      vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
-    }
-  }
-  const uint32_t vt = lds_addr(kv + RG::KB16);
+    for (int u = 0; u < C::KLD; ++u)
+      kr[bb][u] = *reinterpret_cast<const u32x4*>(kv + (bb * C::KLD + u) * 1024 + lane * 16);
+  const uint32_t vt = lds_addr(kv + RG::KB);
   uint32_t va[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
@@ -416,120 +548,235 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, FP8>& S, const unsign
   for (int bb = 0; bb < 2; ++bb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < CB::KLD; ++u) acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[bb][u]), S.q[u], acc);
-    sc[bb] = FP8 ? acc * ksc[bb] : acc;
+    for (int u = 0; u < C::KLD; ++u)
+      acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[bb][u]), S.Q.q[u], acc);
+    sc[bb] = acc;
   }
-
-  // ---- Masks, only for chunks not wholly inside every row's visible range:
-  // scores of invisible keys become -inf; V^T entries (and FP8 V scales) of
-  // tokens outside the item's valid range become 0, since their pool slots
-  // may hold anything, NaN included.
-  const bool fast = (tok0 >= tv0) && (tok0 + kChunk <= tv1) && (tok0 + kChunk - 1 <= L - q) &&
-                    (W == 0 || tok0 > L - 1 - W);
-  if (!fast) {
+  if (!chunk_interior(tok0, tv0, tv1, L, q, W)) {
     // A real branch: the compiler would otherwise turn the selects into
     // straight-line code that every chunk pays for.
     asm volatile("");
-    const int p = S.prow;
+    mask_scores<D, false>(S, sc, tok0, tv0, tv1, W, c);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = tok0 + 16 * bb + 4 * c + i;
-        const bool ok = (j >= tv0) && (j < tv1);
-        const bool vis = ok && (j <= p) && (W == 0 || j > p - W);
-        sc[bb][i] = vis ? sc[bb][i] : -INFINITY;
-        if constexpr (FP8) vs[bb][i] = ok ? vs[bb][i] : 0.f;
+        const bool ok = (j >= tv0) && (j < tv1);  // V of other tokens may be NaN
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)
           vops[mt][4 * bb + i] = ok ? vops[mt][4 * bb + i] : (__bf16)0.f;
       }
     }
   }
-
-  // ---- Online softmax in the exp2 domain (x = s * sigma * log2 e).
-  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  mx = xlane_max4(mx) * scale_log2;
-  if (__any(mx > S.m + kRescale)) {
-    asm volatile("");  // a real branch (rescaling is rare)
-    const float mnew = fmaxf(S.m, mx);
-    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
-    S.m = mnew;
-    S.l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] *= alpha;
-  }
-  // P enters the PV product as two bf16 terms, hi = bf16(p) and
-  // lo = bf16(p - hi), so its rounding error (about 2^-17 relative) stays far
-  // below the output's own bf16 rounding even when one key dominates a row.
-  const float msafe = (S.m == -INFINITY) ? 0.f : S.m;
+  const f32x4 vs[2] = {};
+  float pw[8];
+  softmax_p<D, false>(S, sc, vs, scale_log2, pw);
   bf16x8 p_hi, p_lo;
-  float ps = 0.f;
+  split_bf16(pw, p_hi, p_lo);
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(__builtin_fmaf(sc[bb][i], scale_log2, -msafe));
-      ps += p;
-      const float pw = FP8 ? p * vs[bb][i] : p;
-      const __bf16 hi = (__bf16)pw;
-      p_hi[4 * bb + i] = hi;
-      p_lo[4 * bb + i] = (__bf16)(pw - (float)hi);
-    }
-  }
-  S.l += ps;
-
-  // ---- O^T[d][row] += V^T[d][token] P^T[token][row]. The contraction index
-  // (lane group c, element e) is token 16 (e / 4) + 4 c + e % 4 for both
-  // operands: that is where the S^T accumulator left P.
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) {
-    S.o[mt] = mfma_bf16(vops[mt], p_hi, S.o[mt]);
-    S.o[mt] = mfma_bf16(vops[mt], p_lo, S.o[mt]);
-  }
+  for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = pv_tile(vops[mt], p_hi, p_lo, S.o[mt]);
 }
 
-// FP8: the group's four waves convert the chunk in stage `st` to bf16 in
-// the group's buffer `buf`, exactly, each a quarter of it. K: wave r takes
-// 1 KiB block r of the stage (16 codes per lane = contraction steps 2u and
-// 2u + 1 of one token, which land in bf16 blocks 2u and 2u + 1). V: lane l
-// of wave r takes 16-byte chunk 64 r + l of the FP8 tile (16 columns of one
-// token), which lands as two bf16 chunks in the bf16 swizzle. LDS reads and
-// writes are issued from asm, so that the compiler does not hold them back
-// for the ring's in-flight loads.
+// V^T operands of one FP8 chunk: ds_read_b64_tr_b8 gives lane i of a
+// 16-lane group column i of an 8 x 16 byte tile whose row r the lanes 2r,
+// 2r + 1 address; the group's rows are its 8 tokens 16 (r / 4) + 4 c + r % 4,
+// the contraction order of P^T. One asm block, ending with lgkmcnt(0).
+template <int N>
+__device__ __forceinline__ void vt_reads_b8(i32x2 (&r)[N], const uint32_t (&a)[N]);
+
+template <>
+__device__ __forceinline__ void vt_reads_b8<4>(i32x2 (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4\n\t"
+      "ds_read_b64_tr_b8 %1, %5\n\t"
+      "ds_read_b64_tr_b8 %2, %6\n\t"
+      "ds_read_b64_tr_b8 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void vt_reads_b8<8>(i32x2 (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %8\n\t"
+      "ds_read_b64_tr_b8 %1, %9\n\t"
+      "ds_read_b64_tr_b8 %2, %10\n\t"
+      "ds_read_b64_tr_b8 %3, %11\n\t"
+      "ds_read_b64_tr_b8 %4, %12\n\t"
+      "ds_read_b64_tr_b8 %5, %13\n\t"
+      "ds_read_b64_tr_b8 %6, %14\n\t"
+      "ds_read_b64_tr_b8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void vt_reads_b8<16>(i32x2 (&r)[16], const uint32_t (&a)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %16\n\t"
+      "ds_read_b64_tr_b8 %1, %17\n\t"
+      "ds_read_b64_tr_b8 %2, %18\n\t"
+      "ds_read_b64_tr_b8 %3, %19\n\t"
+      "ds_read_b64_tr_b8 %4, %20\n\t"
+      "ds_read_b64_tr_b8 %5, %21\n\t"
+      "ds_read_b64_tr_b8 %6, %22\n\t"
+      "ds_read_b64_tr_b8 %7, %23\n\t"
+      "ds_read_b64_tr_b8 %8, %24\n\t"
+      "ds_read_b64_tr_b8 %9, %25\n\t"
+      "ds_read_b64_tr_b8 %10, %26\n\t"
+      "ds_read_b64_tr_b8 %11, %27\n\t"
+      "ds_read_b64_tr_b8 %12, %28\n\t"
+      "ds_read_b64_tr_b8 %13, %29\n\t"
+      "ds_read_b64_tr_b8 %14, %30\n\t"
+      "ds_read_b64_tr_b8 %15, %31\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]),
+        "v"(a[15])
+      : "memory");
+}
+
+// The FP8 MFMA: S^T (16 tokens x 16 rows) += K codes x query codes over 128
+// values of d, both e4m3, unscaled.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
+// One chunk for the wave's 16-row tile, FP8 KV, straight from the ring stage
+// st (K codes in the FP8 MFMA's operand order, the V code tile, then the K
+// and V scales). Scores: S^T = K Q^T on the codes, once with each query
+// term, times the per-token K scale and the row's query scale. V^T: the
+// transposing byte reads, issued while the QK products run, converted
+// exactly to bf16 one output tile at a time.
 template <int D>
-__device__ __forceinline__ void convert_chunk(const unsigned char* st, unsigned char* buf, int r,
-                                              int lane) {
-  using C8 = Cfg<D, true>;
-  using CB = Cfg<D, false>;
+__device__ __forceinline__ void compute_chunk(WaveState<D, true>& S, const unsigned char* st,
+                                              int tok0, int tv0, int tv1, int L, int q, int W,
+                                              float scale_log2, int lane) {
+  using C = Cfg<D, true>;
   using RG = Ring<D, true>;
-  constexpr int KBLK = 2 * C8::KLD;   // FP8 K blocks per chunk (4 for D 128, 2 for D 64)
-  constexpr int VCH = kChunk * D / 16; // FP8 V chunks of 16 bytes (256 / 128)
-  u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-  const bool kdo = r < KBLK;
-  const int x = r * 64 + lane;
-  const bool vdo = x < VCH;
-  const int t = x / (D / 16), j = x % (D / 16);
-  const uint32_t ksrc = lds_addr(st + r * 1024 + lane * 16);
-  const uint32_t vsrc = lds_addr(st + RG::KB + t * C8::ROWB + ((j ^ vswz<D, true>(t)) << 4));
-  if (kdo) asm volatile("ds_read_b128 %0, %1" : "=v"(kw) : "v"(ksrc) : "memory");
-  if (vdo) asm volatile("ds_read_b128 %0, %1" : "=v"(vw) : "v"(vsrc) : "memory");
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kw), "+v"(vw) :: "memory");
-  if (kdo) {
-    const int bb = r / C8::KLD, u = r % C8::KLD;
-    const bf16x8 lo = fp8x8_to_bf16(kw[0], kw[1]), hi = fp8x8_to_bf16(kw[2], kw[3]);
-    const uint32_t d0 = lds_addr(buf + (bb * CB::KLD + 2 * u) * 1024 + lane * 16);
-    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024"
-                 :: "v"(d0), "v"(lo), "v"(hi) : "memory");
+  const int c = lane >> 4;
+  const int i16 = lane & 15;
+  const unsigned char* scl = st + RG::KB + RG::VB;
+
+  // ---- S^T = K Q^T, the K operands read page by page.
+  f32x4 sc[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS8; ++ks) {
+      u32x4 x0, x1;
+      if constexpr (D >= 128) {
+        x0 = *reinterpret_cast<const u32x4*>(st + (bb * C::KLD + 2 * ks) * 1024 + lane * 16);
+        x1 = *reinterpret_cast<const u32x4*>(st + (bb * C::KLD + 2 * ks + 1) * 1024 + lane * 16);
+      } else {
+        // D 64: d = 32 c + 0..15 and + 16..31 sit with lane groups 2c and
+        // 2c + 1 of the page's one load; groups 2 and 3 carry zeros.
+        const int cc = (2 * c) & 3;
+        x0 = *reinterpret_cast<const u32x4*>(st + bb * 1024 + (i16 + 16 * cc) * 16);
+        x1 = *reinterpret_cast<const u32x4*>(st + bb * 1024 + (i16 + 16 * (cc + 1)) * 16);
+        if (c >= 2) x0 = x1 = u32x4{0, 0, 0, 0};
+      }
+      const i32x8 kop = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      acc = mfma_fp8(kop, S.Q.hi[ks], acc);
+      acc = mfma_fp8(kop, S.Q.lo[ks], acc);
+    }
+    sc[bb] = acc;
   }
-  if (vdo) {
-    const bf16x8 lo = fp8x8_to_bf16(vw[0], vw[1]), hi = fp8x8_to_bf16(vw[2], vw[3]);
-    unsigned char* vb = buf + RG::KB16;
-    const uint32_t d0 = lds_addr(vb + vtile_chunk<D, false>(t, 2 * j));
-    const uint32_t d1 = lds_addr(vb + vtile_chunk<D, false>(t, 2 * j + 1));
-    asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3"
-                 :: "v"(d0), "v"(d1), "v"(lo), "v"(hi) : "memory");
+  f32x4 ksc[2], vs[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    ksc[bb] = *reinterpret_cast<const f32x4*>(scl + (bb * 16 + 4 * c) * 4);
+    vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
+  }
+
+  // ---- V code columns: lanes 2r, 2r + 1 of a group address token
+  // 16 (r / 4) + 4 c + r % 4 (the P^T order), bytes 16 mt + 8 k. The stage
+  // and the token row are 256-byte and ROWB aligned and the swizzle only
+  // touches the 16-byte chunk bits, so tile mt's address is a fixed XOR of
+  // one base.
+  i32x2 vcode[C::MT];
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // keep the per-tile addresses out of the loop
+    const int rr = (ln & 15) >> 1, k = ln & 1;
+    const int t = 16 * (rr >> 2) + 4 * (ln >> 4) + (rr & 3);
+    const uint32_t vbase = lds_addr(st + RG::KB) + t * C::ROWB + (vswz<D, true>(t) << 4) + 8 * k;
+    uint32_t va[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) va[mt] = vbase ^ (uint32_t)(mt << 4);
+    vt_reads_b8<C::MT>(vcode, va);
+  }
+
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) sc[bb] = sc[bb] * (ksc[bb] * S.Q.qs);
+  const bool interior = chunk_interior(tok0, tv0, tv1, L, q, W);
+  if (!interior) {
+    asm volatile("");  // a real branch
+    mask_scores<D, true>(S, sc, tok0, tv0, tv1, W, c);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = tok0 + 16 * bb + 4 * c + i;
+        vs[bb][i] = ((j >= tv0) && (j < tv1)) ? vs[bb][i] : 0.f;  // NaN scales of other slots
+      }
+    }
+  }
+  float pw[8];
+  softmax_p<D, true>(S, sc, vs, scale_log2, pw);
+  if (!interior) {
+    asm volatile("");
+    // Codes of tokens outside the item's range become 0 (byte e of a
+    // column is token 16 (e / 4) + 4 c + e % 4).
+    uint32_t keep[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      keep[bb] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = tok0 + 16 * bb + 4 * c + i;
+        keep[bb] |= ((j >= tv0) && (j < tv1)) ? (0xFFu << (8 * i)) : 0u;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      vcode[mt][0] &= (int)keep[0];
+      vcode[mt][1] &= (int)keep[1];
+    }
+  }
+  // PV in fp16: V codes convert exactly, p w (< 2^14 w) rounds to 11 bits,
+  // one product per output tile. A V scale above 2 (p w could pass fp16's
+  // range) takes the bf16 hi + lo form instead.
+  const bool wide = __any(fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
+                                fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3]))) >
+                          2.0f);
+  if (!wide) {
+    f16x8 p16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p16[e] = (_Float16)pw[e];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      S.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          fp8x8_to_f16((uint32_t)vcode[mt][0], (uint32_t)vcode[mt][1]), p16, S.o[mt], 0, 0, 0);
+  } else {
+    asm volatile("");  // a real branch
+    bf16x8 p_hi, p_lo;
+    split_bf16(pw, p_hi, p_lo);
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      S.o[mt] = pv_tile(fp8x8_to_bf16((uint32_t)vcode[mt][0], (uint32_t)vcode[mt][1]), p_hi, p_lo,
+                        S.o[mt]);
   }
 }
 
@@ -551,8 +798,71 @@ __device__ __forceinline__ float sink_log2(const KernelArgs& A, int b, int h) {
   return -INFINITY;
 }
 
+// The lane's query values for the FP8 MFMA: the 32 values d = 128 ks +
+// 32 c + j of its row (zeros past D), as two e4m3 terms of the row scaled by
+// a power of two, Q = qs (hi + lo). With the row's largest |value| scaled
+// into [128, 256), hi keeps the top 4 significant bits and the exact
+// residual fits lo's 4 bits for every value within 2^-9 of the row's
+// largest (bf16 values carry 8 significant bits), so the two terms
+// reproduce Q exactly there and to within 2^-17 of the row's largest
+// value below that.
+template <int D>
+__device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t* qp, bool live,
+                                               int c) {
+  using C = Cfg<D, true>;
+  u32x4 raw[C::KS8][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS8; ++ks) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int d = 128 * ks + 32 * c + 8 * v;
+      raw[ks][v] = u32x4{0, 0, 0, 0};
+      if (live && d < D) raw[ks][v] = *reinterpret_cast<const u32x4*>(qp + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(raw[ks][v][e] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(raw[ks][v][e] & 0xFFFF0000u)));
+      }
+    }
+  }
+  amax = xlane_max4(amax);
+  // 2^e <= amax < 2^(e+1); a zero (or subnormal) row keeps e >= -100.
+  int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;
+  e = e < -100 ? -100 : e;
+  const float inv = __uint_as_float((uint32_t)(127 + 7 - e) << 23);  // 2^(7 - e)
+  Q.qs = __uint_as_float((uint32_t)(127 - 7 + e) << 23);             // 2^(e - 7)
+#pragma unroll
+  for (int ks = 0; ks < C::KS8; ++ks) {
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // dwords 2v, 2v + 1: four values each
+        uint32_t hb = 0, lb = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t w = raw[ks][v][2 * h + (b >> 1)];
+          const float x = __uint_as_float((b & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          const float y = x * inv;
+          const float yh = e4m3_round(y);
+          const float yl = e4m3_round(y - yh);
+          hb |= e4m3_code(yh) << (8 * b);
+          lb |= e4m3_code(yl) << (8 * b);
+        }
+        hw[2 * v + h] = hb;
+        lw[2 * v + h] = lb;
+      }
+    }
+    Q.hi[ks] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3],
+                     (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+    Q.lo[ks] = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3],
+                     (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+  }
+}
+
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A) {
+__global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
   using RG = Ring<D, FP8>;
   __shared__ Smem<D, FP8> sm;
@@ -560,8 +870,8 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int gp = w / kGroupWaves, r = w % kGroupWaves;     // token group, row tile
-  const bool loader = r == kTileWaves;                      // the group's loader
+  const int gp = w / kGroupWaves<D>, r = w % kGroupWaves<D>;  // token group, row tile
+  const bool loader = r == kTileWaves<D>;                      // the group's loader
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
@@ -577,7 +887,7 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
   // Page ids of every chunk (a page past the item's end repeats the
   // chunk's first page, whose slots the masks then exclude).
   const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
-  for (int i = tid; i < 2 * nch; i += kThreads) {
+  for (int i = tid; i < 2 * nch; i += kThreads<D>) {
     const int k = i >> 1, which = i & 1;
     const int tok0 = tokbase + k * kChunk;
     const int pg = (tok0 >> 4) + which;
@@ -596,11 +906,15 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
     S.m = -INFINITY;
     S.l = 0.f;
     const uint16_t* qp = A.q + ((int64_t)(it.q_off + i) * Hq + g * G + hh) * D;
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      u32x4 v = {0, 0, 0, 0};
-      if (live) v = *reinterpret_cast<const u32x4*>(qp + qk_dmap<D, FP8>(s, c));
-      S.q[s] = __builtin_bit_cast(bf16x8, v);
+      for (int s = 0; s < C::KS; ++s) {
+        u32x4 v = {0, 0, 0, 0};
+        if (live) v = *reinterpret_cast<const u32x4*>(qp + qk_dmap(s, c));
+        S.Q.q[s] = __builtin_bit_cast(bf16x8, v);
+      }
+    } else {
+      load_query_fp8<D>(S.Q, qp, live, c);
     }
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -626,22 +940,9 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
       issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, lane);
     }
   }
-  unsigned char* cbuf = ring + RG::R * RG::STAGE;  // FP8: bf16 copies [2][COPY]
-  if constexpr (FP8) {
-    // The first chunk's copy, before the loop: wait for its stage (the next
-    // R - 2 stages may be pending), barrier, convert.
-    if (loader) {
-      if (gp + kGroups * (RG::R - 2) < nch) wait_vm<RG::WAIT0>();
-      else wait_vm<0>();
-    }
-    ring_barrier();
-    if (gp < nch) convert_chunk<D>(ring, cbuf, r, lane);
-  }
   for (int k = 0; k < nst; ++k) {
     const int ck = gp + kGroups * k;
-    if (loader) {
-      // bf16: this step's chunk has landed; FP8: the next one too (it is
-      // converted during this step).
+    if (loader) {  // this step's chunk has landed; the next R - 2 may be pending
       if (gp + kGroups * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
       else wait_vm<0>();
     }
@@ -652,22 +953,9 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
       chunk_pages(pages_addr, cn, pa, pb);
       issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, lane);
     }
-    const unsigned char* st = ring + (k % RG::R) * RG::STAGE;
-    if constexpr (FP8) {
-      // Convert the next chunk into the other copy (whose last reader, the
-      // previous step's compute, finished before the barrier above), then
-      // compute on this step's copy (converted during the previous step).
-      if (ck + kGroups < nch)
-        convert_chunk<D>(ring + ((k + 1) % RG::R) * RG::STAGE, cbuf + ((k + 1) & 1) * RG::COPY,
-                         r, lane);
-      if (active && ck < nch)
-        compute_chunk<D, FP8>(S, cbuf + (k & 1) * RG::COPY, st + RG::KB + RG::VB,
-                              tokbase + ck * kChunk, tv0, tv1, L, q, W, A.scale_log2, lane);
-    } else {
-      if (active && ck < nch)
-        compute_chunk<D, FP8>(S, st, nullptr, tokbase + ck * kChunk, tv0, tv1, L, q, W,
-                              A.scale_log2, lane);
-    }
+    if (active && ck < nch)
+      compute_chunk<D>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1, L, q,
+                       W, A.scale_log2, lane);
   }
 
   // ---- Merge the groups: group 1's waves hand (m, l, O) of their tile to
@@ -676,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void pa_partition_kernel(KernelArgs A)
   S.l = xlane_sum4(S.l);
   __syncthreads();
   f32x4* xo = reinterpret_cast<f32x4*>(&sm.ring[0][0]);       // [tile][mt][lane]
-  float* xm = reinterpret_cast<float*>(&sm.ring[0][0]) + kGroupWaves * C::MT * 64 * 4;  // [tile][lane][m, l]
+  float* xm = reinterpret_cast<float*>(&sm.ring[0][0]) + kTileWaves<D> * C::MT * 64 * 4;  // [tile][lane][m, l]
   if (gp == 1 && active) {
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) xo[(r * C::MT + mt) * 64 + lane] = S.o[mt];
@@ -804,8 +1092,14 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (ntmax < 1 || ntmax > kGroupWaves) return hipErrorInvalidValue;
-  dim3 grid(n_items), block(kThreads);
+  const dim3 grid(n_items);
+  if (head_dim == 256) {  // FP8 KV only, at most 48 rows
+    if (!fp8 || ntmax < 1 || ntmax > kTileWaves<256>) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_partition_kernel<256, true>), grid, dim3(kThreads<256>), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (ntmax < 1 || ntmax > kTileWaves<128>) return hipErrorInvalidValue;
+  const dim3 block(kThreads<128>);
   if (head_dim == 128) {
     if (fp8) hipLaunchKernelGGL((pa_partition_kernel<128, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((pa_partition_kernel<128, false>), grid, block, 0, stream, a);
@@ -820,13 +1114,17 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
                          int max_parts, hipStream_t stream) {
   if (n_red <= 0) return hipSuccess;
   const unsigned items = (unsigned)n_red * rows_stride;
-  if (max_parts <= 32) {  // one workgroup per row: 32 (D 128) or 16 column lanes x 4 or 8
-    if (head_dim == 128)
+  if (max_parts <= 32) {  // 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
+    if (head_dim == 256)    // half a row per workgroup
+      hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4>), dim3(items * 2), dim3(128), 0, stream, a);
+    else if (head_dim == 128)
       hipLaunchKernelGGL((pa_reduce_kernel<128, 32, 4>), dim3(items), dim3(128), 0, stream, a);
     else
       hipLaunchKernelGGL((pa_reduce_kernel<64, 16, 8>), dim3(items), dim3(128), 0, stream, a);
-  } else {  // 8 column lanes x 32 partition lanes per quarter (or half) of a row
-    if (head_dim == 128)
+  } else {  // 8 column lanes x 32 partition lanes per eighth, quarter or half of a row
+    if (head_dim == 256)
+      hipLaunchKernelGGL((pa_reduce_kernel<256, 8, 32>), dim3(items * 8), dim3(256), 0, stream, a);
+    else if (head_dim == 128)
       hipLaunchKernelGGL((pa_reduce_kernel<128, 8, 32>), dim3(items * 4), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((pa_reduce_kernel<64, 8, 32>), dim3(items * 2), dim3(256), 0, stream, a);

@@ -115,8 +115,10 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
                 s->num_q_heads, s->num_kv_heads);
   if (s->block_size != kBlock)
     return fail(PA_E_UNSUPPORTED, "block_size %d: only 16-token blocks are served", s->block_size);
-  if (s->head_dim != 64 && s->head_dim != 128)
-    return fail(PA_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are served", s->head_dim);
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256)
+    return fail(PA_E_UNSUPPORTED, "head_dim %d: only 64, 128 and 256 are served", s->head_dim);
+  if (s->head_dim == 256 && s->kv_dtype != PA_FP8_E4M3)
+    return fail(PA_E_UNSUPPORTED, "head_dim 256 is served for FP8 e4m3 KV only");
   if (s->q_dtype != PA_BF16) return fail(PA_E_UNSUPPORTED, "q_dtype must be bf16");
   if (s->kv_dtype != PA_BF16 && s->kv_dtype != PA_FP8_E4M3)
     return fail(PA_E_UNSUPPORTED, "kv_dtype must be bf16 or fp8 e4m3");
@@ -155,10 +157,11 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
       return fail(PA_E_INVALID, "context_lens[%d] = %d needs more blocks than the pool holds", b,
                   L);
     if (win && win[b] < 0) return fail(PA_E_INVALID, "window[%d] = %d < 0", b, win[b]);
-    if (q * G > kMaxRows)
+    const int max_rows = s->head_dim == 256 ? kMaxRows256 : kMaxRows;
+    if (q * G > max_rows)
       return fail(PA_E_UNSUPPORTED,
-                  "sequence %d packs %d x %d = %d rows per KV head; at most %d are served", b, q,
-                  G, q * G, kMaxRows);
+                  "sequence %d packs %d x %d = %d rows per KV head; at most %d are served at "
+                  "head_dim %d", b, q, G, q * G, max_rows, s->head_dim);
     total_q += q;
   }
   if (total_q * s->num_q_heads * (int64_t)s->head_dim > ((int64_t)1 << 40))

@@ -51,7 +51,9 @@ REFUSALS = [
     # (shape overrides, ctx, q, window, expected status, message fragment)
     (dict(block_size=32), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "block_size"),
     (dict(head_dim=96), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "head_dim"),
-    (dict(head_dim=256), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "head_dim"),
+    (dict(head_dim=256), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "FP8"),
+    (dict(head_dim=256, kv_dtype="fp8", num_q_heads=16, num_kv_heads=2), [100, 50], [8, 6],
+     None, pav.PA_E_UNSUPPORTED, "at most 48"),
     (dict(num_q_heads=15), [100, 50], [6, 6], None, pav.PA_E_INVALID, "multiple"),
     (dict(num_seqs=0), [], [], None, pav.PA_E_INVALID, "num_seqs"),
     (dict(kv_dtype="fp32"), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "kv_dtype"),
@@ -186,6 +188,18 @@ def test_long_context_partitions():
     assert info["kv_bytes"] == 2 * (1 << 20) * 512
     # partials: one (rows x (D + 2)) fp32 record per item
     assert info["scratch_bytes"] == info["work_items"] * 48 * (128 + 2) * 4
+    plan.close()
+
+
+def test_head256_worklist_at_full_size():
+    shape = base_shape(num_seqs=8, num_q_heads=8, num_kv_heads=1, head_dim=256, kv_dtype="fp8",
+                       num_blocks=150000, max_blocks_per_seq=9375, softmax_scale=0.0625)
+    ctx, q = [150000] * 8, [6] * 8
+    plan = pav.pa_plan(shape, ctx, q, None, device=-1)
+    check_worklist(plan, ctx, q, None, 1)
+    info = plan.info()
+    assert info["kv_bytes"] == 8 * 150000 * (2 * 256 + 8)
+    assert info["work_items"] <= 256  # one round of the device's CUs
     plan.close()
 
 

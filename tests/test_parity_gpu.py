@@ -148,6 +148,18 @@ def test_mixed_ragged_full():
     check(workloads.make(5), "workload 5 full", strict=True)
 
 
+@pytest.mark.parametrize("P", [None, 64, 512])
+def test_head256_reduced(P):
+    check(workloads.make(6, scale_ctx=1 / 32, num_seqs=4), f"workload 6 reduced P={P}",
+          partition_tokens=P)
+
+
+def test_head256_full_one_sequence():
+    """The head-256 shape at its full 150,000-token context (batch 1), in the
+    bench's launch configuration."""
+    check(workloads.make(6, num_seqs=1), "workload 6 full, batch 1", strict=True)
+
+
 @pytest.mark.parametrize("P", [None, 512])
 def test_long_context_full_sampled(P):
     wl = workloads.make(4)
@@ -189,6 +201,15 @@ EDGES = {
     "FP8 with windows and sinks": dict(kv_dtype="fp8", ctx_lens=[2500, 300], q_lens=[6, 8],
                                        window=[1000, 0], sinks_rows=[True, True]),
     "bf16 output": dict(out_dtype="bf16", ctx_lens=[1200, 17], q_lens=[6, 6]),
+    "head dim 256, FP8, ragged": dict(head_dim=256, kv_dtype="fp8", num_q_heads=8,
+                                      num_kv_heads=1, ctx_lens=[700, 129, 33, 16, 6],
+                                      q_lens=[6, 1, 5, 3, 6]),
+    "head dim 256, FP8, windows and sinks": dict(
+        head_dim=256, kv_dtype="fp8", num_q_heads=8, num_kv_heads=1, ctx_lens=[2500, 300, 90],
+        q_lens=[6, 4, 2], window=[1000, 0, 7], sinks_rows=[True, True, False]),
+    "head dim 256, FP8, two KV heads, q 8": dict(
+        head_dim=256, kv_dtype="fp8", num_q_heads=12, num_kv_heads=2, ctx_lens=[1500, 77],
+        q_lens=[8, 8]),
 }
 
 

@@ -325,11 +325,24 @@ CONFIG_NAMES = {
     3: "per-token FP8 KV: B32 q4/6 16q/2kv D128 L~U[1024,16384] e4m3",
     4: "long context: B1 q6 16q/2kv D128 L=1048576 bf16, 512-token partitions",
     5: "mixed ragged: B128 q~U{1..8} 16q/2kv D128 L~lognormal(8K) FP8, 1/4 windowed+sinks",
+    6: "head-256 FP8 verify: B8 q6 8q/1kv D256 L=150000 e4m3 (first 1/2/4/8 sequences)",
 }
 
 
 def default_seed(config: int) -> int:
     return 1000 + config
+
+
+def first_seqs(wl: Workload, n: int) -> Workload:
+    """The workload restricted to its first n sequences (same pools)."""
+    t = int(wl.q_lens[:n].sum())
+    return dataclasses.replace(
+        wl, name=f"{wl.name}, first {n}", num_seqs=n, ctx_lens=wl.ctx_lens[:n].clone(),
+        q_lens=wl.q_lens[:n].clone(), q=wl.q[:t].contiguous(),
+        window=None if wl.window is None else wl.window[:n].clone(),
+        block_table=wl.block_table[:n].contiguous(),
+        sinks=(wl.sinks[:n].contiguous() if wl.sinks is not None and wl.sinks_mode == 2
+               else wl.sinks))
 
 
 def _uniform_int(gen: torch.Generator, lo: int, hi: int, n: int) -> list[int]:
@@ -385,6 +398,13 @@ def make(config: int, seed: Optional[int] = None, *, scale_ctx: float = 1.0,
                   head_dim=128, kv_dtype="fp8", out_dtype="bf16",
                   window=[win_tokens if w else 0 for w in windowed],
                   sinks_rows=windowed)
+    elif config == 6:
+        # One rank's share at the head-256 kernel microbenchmark shape: 8 q
+        # heads over 1 KV head, q = 6 (48 rows), every context 150,000
+        # tokens; the batch sizes 1/2/4/8 are the first sequences of this one.
+        B = num_seqs or 8
+        kw = dict(ctx_lens=[sc(150000)] * B, q_lens=[6] * B, num_q_heads=8, num_kv_heads=1,
+                  head_dim=256, kv_dtype="fp8", out_dtype="bf16")
     else:
         raise ValueError(f"unknown workload {config}")
     kw.update(overrides)
