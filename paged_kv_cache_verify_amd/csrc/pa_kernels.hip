@@ -138,6 +138,20 @@ __device__ __forceinline__ float xlane_sum4(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one instruction. (fmaxf would first quiet possible
+// signalling NaNs with an extra instruction per operand; the operands here
+// are scores and scales, never NaN where they are used.)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float max8(const f32x4 (&x)[2]) {
+  return max3(max3(x[0][0], x[0][1], x[0][2]), max3(x[0][3], x[1][0], x[1][1]),
+              __builtin_fmaxf(x[1][2], x[1][3]));
+}
+
 // LDS V tile of one wave: [32 tokens][D] elements (bf16, or FP8 codes),
 // token-major, stored in 16-byte chunks whose position within a token row is
 // XOR-swizzled by the token, so that the transposing reads below (16 lanes
@@ -204,11 +218,21 @@ struct Ring {
   static_assert(STAGE % 256 == 0 && KB % 256 == 0, "stage addresses keep their low 8 bits zero");
 };
 
+// FP8 at D 256 keeps the query operands of each row tile in LDS (both
+// token groups read the same tile), which frees 32 registers per compute
+// wave: the accumulators then stay in place across the loop. Per tile: the
+// two terms of the two contraction steps, 2 KiB each, in lane order.
+template <int D, bool FP8>
+constexpr bool kQInLds = FP8 && D == 256;
+template <int D, bool FP8>
+constexpr int kQBytes = kQInLds<D, FP8> ? kTileWaves<D> * 4 * 2048 : 16;
+
 // The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
 // FP8 V reads rely on the low 8 bits of a stage's address being zero.
 template <int D, bool FP8>
 struct Smem {
   alignas(1024) unsigned char ring[kGroups][Ring<D, FP8>::RING];
+  alignas(16) unsigned char qbuf[kQBytes<D, FP8>];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
@@ -431,23 +455,39 @@ __device__ __forceinline__ void mask_scores(const WaveState<D, FP8>& S, f32x4 (&
 // probabilities clear of fp16's subnormal range. Adds the chunk's
 // probabilities to l and returns p w per score element, w the token's V scale
 // (FP8) or 1.
+//
+// FP8: `extra` (>= 0, log2 units) raises the chunk's largest x for that test,
+// so that a chunk whose V scales reach 2^(1 + extra) still keeps p w below
+// 2^15.
+template <bool FP8>
+constexpr float kShift = FP8 ? 6.0f : 0.0f;
+
+// The chunk's largest x per row (plus `extra`), and whether any row must move
+// its reference.
 template <int D, bool FP8>
-__device__ __forceinline__ void softmax_p(WaveState<D, FP8>& S, const f32x4 (&sc)[2],
-                                          const f32x4 (&vs)[2], float scale_log2, float (&pw)[8]) {
+__device__ __forceinline__ bool needs_rescale(const WaveState<D, FP8>& S, const f32x4 (&sc)[2],
+                                              float scale_log2, float extra, float& mx) {
+  mx = xlane_max4(max8(sc)) * scale_log2 + extra;
+  return __any(mx > S.m + (kShift<FP8> + kRescale));
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void rescale(WaveState<D, FP8>& S, float mx) {
   using C = Cfg<D, FP8>;
-  constexpr float kShift = FP8 ? 6.0f : 0.0f;
-  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  mx = xlane_max4(mx) * scale_log2;
-  if (__any(mx > S.m + (kShift + kRescale))) {
-    asm volatile("");  // a real branch (rescaling is rare)
-    const float mnew = fmaxf(S.m, mx - kShift);
-    const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
-    S.m = mnew;
-    S.l *= alpha;
+  const float mnew = fmaxf(S.m, mx - kShift<FP8>);
+  const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(S.m - mnew);
+  S.m = mnew;
+  S.l *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] *= alpha;
-  }
+  for (int mt = 0; mt < C::MT; ++mt) S.o[mt] *= alpha;
+}
+
+// The chunk's probabilities for the current reference: adds them to l and
+// returns p w per score element.
+template <int D, bool FP8>
+__device__ __forceinline__ void chunk_probs(WaveState<D, FP8>& S, const f32x4 (&sc)[2],
+                                            const f32x4 (&vs)[2], float scale_log2,
+                                            float (&pw)[8]) {
   const float msafe = (S.m == -INFINITY) ? 0.f : S.m;
   float ps = 0.f;
 #pragma unroll
@@ -460,6 +500,18 @@ __device__ __forceinline__ void softmax_p(WaveState<D, FP8>& S, const f32x4 (&sc
     }
   }
   S.l += ps;
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void softmax_p(WaveState<D, FP8>& S, const f32x4 (&sc)[2],
+                                          const f32x4 (&vs)[2], float scale_log2, float (&pw)[8],
+                                          float extra = 0.f) {
+  float mx;
+  if (needs_rescale(S, sc, scale_log2, extra, mx)) {
+    asm volatile("");  // a real branch (rescaling is rare)
+    rescale(S, mx);
+  }
+  chunk_probs(S, sc, vs, scale_log2, pw);
 }
 
 // P^T as two bf16 terms, hi = bf16(p w) and lo = bf16(p w - hi): its
@@ -509,7 +561,8 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 template <int D>
 __device__ __forceinline__ void compute_chunk(WaveState<D, false>& S, const unsigned char* kv,
                                               int tok0, int tv0, int tv1, int L, int q, int W,
-                                              float scale_log2, int lane) {
+                                              float scale_log2, int lane,
+                                              const unsigned char* = nullptr) {
   using C = Cfg<D, false>;
   using RG = Ring<D, false>;
   const int c = lane >> 4;
@@ -651,24 +704,38 @@ __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 acc) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
 }
 
-// One chunk for the wave's 16-row tile, FP8 KV, straight from the ring stage
-// st (K codes in the FP8 MFMA's operand order, the V code tile, then the K
-// and V scales). Scores: S^T = K Q^T on the codes, once with each query
-// term, times the per-token K scale and the row's query scale. V^T: the
-// transposing byte reads, issued while the QK products run, converted
-// exactly to bf16 one output tile at a time.
+// One chunk of FP8 KV for the wave's 16-row tile between its two phases:
+// the scores (masked, in score units), the V scales, the V code columns and
+// the chunk's largest x per row.
 template <int D>
-__device__ __forceinline__ void compute_chunk(WaveState<D, true>& S, const unsigned char* st,
-                                              int tok0, int tv0, int tv1, int L, int q, int W,
-                                              float scale_log2, int lane) {
+struct Fp8Chunk {
+  f32x4 sc[2];
+  f32x4 vs[2];
+  i32x2 vcode[Cfg<D, true>::MT];
+  float mx;
+  int tok0;
+  bool interior;
+};
+
+// Phase 1 of an FP8 chunk, straight from the ring stage st (K codes in the
+// FP8 MFMA's operand order, the V code tile, then the K and V scales):
+// S^T = K Q^T on the codes, once with each query term, times the per-token
+// K scale and the row's query scale; masks; the V code columns (transposing
+// byte reads, issued while the QK products run). Returns whether a row's
+// reference must move before the chunk's probabilities are taken.
+template <int D>
+__device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chunk<D>& X,
+                                             const unsigned char* st, int tok0, int tv0, int tv1,
+                                             int L, int q, int W, float scale_log2, int lane,
+                                             const unsigned char* qb) {
   using C = Cfg<D, true>;
   using RG = Ring<D, true>;
   const int c = lane >> 4;
   const int i16 = lane & 15;
   const unsigned char* scl = st + RG::KB + RG::VB;
+  X.tok0 = tok0;
 
   // ---- S^T = K Q^T, the K operands read page by page.
-  f32x4 sc[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -688,54 +755,86 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, true>& S, const unsig
       }
       const i32x8 kop = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      acc = mfma_fp8(kop, S.Q.hi[ks], acc);
-      acc = mfma_fp8(kop, S.Q.lo[ks], acc);
+      if constexpr (kQInLds<D, true>) {
+        const i32x8 qh = *reinterpret_cast<const i32x8*>(qb + (2 * ks) * 2048 + lane * 32);
+        const i32x8 ql = *reinterpret_cast<const i32x8*>(qb + (2 * ks + 1) * 2048 + lane * 32);
+        acc = mfma_fp8(kop, qh, acc);
+        acc = mfma_fp8(kop, ql, acc);
+      } else {
+        acc = mfma_fp8(kop, S.Q.hi[ks], acc);
+        acc = mfma_fp8(kop, S.Q.lo[ks], acc);
+      }
     }
-    sc[bb] = acc;
+    X.sc[bb] = acc;
   }
-  f32x4 ksc[2], vs[2];
+  f32x4 ksc[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     ksc[bb] = *reinterpret_cast<const f32x4*>(scl + (bb * 16 + 4 * c) * 4);
-    vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
+    X.vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
   }
 
   // ---- V code columns: lanes 2r, 2r + 1 of a group address token
   // 16 (r / 4) + 4 c + r % 4 (the P^T order), bytes 16 mt + 8 k. The stage
   // and the token row are 256-byte and ROWB aligned and the swizzle only
   // touches the 16-byte chunk bits, so tile mt's address is a fixed XOR of
-  // one base.
-  i32x2 vcode[C::MT];
+  // one base. (The compute waves issue no direct-to-LDS loads, so the
+  // compiler's own waits around these reads cost nothing.)
   {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keep the per-tile addresses out of the loop
     const int rr = (ln & 15) >> 1, k = ln & 1;
     const int t = 16 * (rr >> 2) + 4 * (ln >> 4) + (rr & 3);
     const uint32_t vbase = lds_addr(st + RG::KB) + t * C::ROWB + (vswz<D, true>(t) << 4) + 8 * k;
-    uint32_t va[C::MT];
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) va[mt] = vbase ^ (uint32_t)(mt << 4);
-    vt_reads_b8<C::MT>(vcode, va);
+    for (int mt = 0; mt < C::MT; ++mt)
+      X.vcode[mt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(uintptr_t)(vbase ^ (uint32_t)(mt << 4)));
   }
 
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) sc[bb] = sc[bb] * (ksc[bb] * S.Q.qs);
-  const bool interior = chunk_interior(tok0, tv0, tv1, L, q, W);
-  if (!interior) {
+  for (int bb = 0; bb < 2; ++bb) X.sc[bb] = X.sc[bb] * (ksc[bb] * S.Q.qs);
+  X.interior = chunk_interior(tok0, tv0, tv1, L, q, W);
+  if (!X.interior) {
     asm volatile("");  // a real branch
-    mask_scores<D, true>(S, sc, tok0, tv0, tv1, W, c);
+    mask_scores<D, true>(S, X.sc, tok0, tv0, tv1, W, c);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = tok0 + 16 * bb + 4 * c + i;
-        vs[bb][i] = ((j >= tv0) && (j < tv1)) ? vs[bb][i] : 0.f;  // NaN scales of other slots
+        X.vs[bb][i] = ((j >= tv0) && (j < tv1)) ? X.vs[bb][i] : 0.f;  // NaN scales of other slots
       }
     }
   }
+  // p w enters an fp16 product: p < 2^14 keeps it below 2^15 while the V
+  // scales stay at most 2; a chunk with a larger V scale w raises the
+  // softmax reference by log2(w) - 1 (rare: |V| above 896).
+  float extra = 0.f;
+  {
+    const float vmax = max3(max3(X.vs[0][0], X.vs[0][1], X.vs[0][2]),
+                            max3(X.vs[0][3], X.vs[1][0], X.vs[1][1]),
+                            __builtin_fmaxf(X.vs[1][2], X.vs[1][3]));
+    if (__any(vmax > 2.0f)) {
+      asm volatile("");  // a real branch
+      extra = __builtin_amdgcn_logf(xlane_max4(vmax)) - 1.0f;
+    }
+  }
+  return needs_rescale(S, X.sc, scale_log2, extra, X.mx);
+}
+
+// Phase 2 of an FP8 chunk: probabilities for the current reference, the V
+// code mask and O^T += V^T P^T in fp16 (V codes convert exactly, p w
+// (< 2^15) rounds to 11 bits: a relative error of at most 2^-12), one
+// product per output tile.
+template <int D>
+__device__ __forceinline__ void chunk_finish(WaveState<D, true>& S, Fp8Chunk<D>& X, int tv0,
+                                             int tv1, float scale_log2, int lane) {
+  using C = Cfg<D, true>;
+  const int c = lane >> 4;
   float pw[8];
-  softmax_p<D, true>(S, sc, vs, scale_log2, pw);
-  if (!interior) {
+  chunk_probs<D, true>(S, X.sc, X.vs, scale_log2, pw);
+  if (!X.interior) {
     asm volatile("");
     // Codes of tokens outside the item's range become 0 (byte e of a
     // column is token 16 (e / 4) + 4 c + e % 4).
@@ -745,39 +844,23 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, true>& S, const unsig
       keep[bb] = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = tok0 + 16 * bb + 4 * c + i;
+        const int j = X.tok0 + 16 * bb + 4 * c + i;
         keep[bb] |= ((j >= tv0) && (j < tv1)) ? (0xFFu << (8 * i)) : 0u;
       }
     }
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      vcode[mt][0] &= (int)keep[0];
-      vcode[mt][1] &= (int)keep[1];
+      X.vcode[mt][0] &= (int)keep[0];
+      X.vcode[mt][1] &= (int)keep[1];
     }
   }
-  // PV in fp16: V codes convert exactly, p w (< 2^14 w) rounds to 11 bits,
-  // one product per output tile. A V scale above 2 (p w could pass fp16's
-  // range) takes the bf16 hi + lo form instead.
-  const bool wide = __any(fmaxf(fmaxf(fmaxf(vs[0][0], vs[0][1]), fmaxf(vs[0][2], vs[0][3])),
-                                fmaxf(fmaxf(vs[1][0], vs[1][1]), fmaxf(vs[1][2], vs[1][3]))) >
-                          2.0f);
-  if (!wide) {
-    f16x8 p16;
+  f16x8 p16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p16[e] = (_Float16)pw[e];
+  for (int e = 0; e < 8; ++e) p16[e] = (_Float16)pw[e];
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      S.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          fp8x8_to_f16((uint32_t)vcode[mt][0], (uint32_t)vcode[mt][1]), p16, S.o[mt], 0, 0, 0);
-  } else {
-    asm volatile("");  // a real branch
-    bf16x8 p_hi, p_lo;
-    split_bf16(pw, p_hi, p_lo);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      S.o[mt] = pv_tile(fp8x8_to_bf16((uint32_t)vcode[mt][0], (uint32_t)vcode[mt][1]), p_hi, p_lo,
-                        S.o[mt]);
-  }
+  for (int mt = 0; mt < C::MT; ++mt)
+    S.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        fp8x8_to_f16((uint32_t)X.vcode[mt][0], (uint32_t)X.vcode[mt][1]), p16, S.o[mt], 0, 0, 0);
 }
 
 template <int D, bool FP8>
@@ -915,6 +998,16 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
       }
     } else {
       load_query_fp8<D>(S.Q, qp, live, c);
+      if constexpr (kQInLds<D, FP8>) {
+        if (gp == 0 && active) {  // both groups' wave r read tile r's operands
+          unsigned char* qb = sm.qbuf + r * 8192 + lane * 32;
+#pragma unroll
+          for (int ks = 0; ks < C::KS8; ++ks) {
+            *reinterpret_cast<i32x8*>(qb + (2 * ks) * 2048) = S.Q.hi[ks];
+            *reinterpret_cast<i32x8*>(qb + (2 * ks + 1) * 2048) = S.Q.lo[ks];
+          }
+        }
+      }
     }
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -940,8 +1033,8 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
       issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, lane);
     }
   }
-  for (int k = 0; k < nst; ++k) {
-    const int ck = gp + kGroups * k;
+  // One step: the loader's wait, the barrier, the loader's refill.
+  auto step_begin = [&](int k) __attribute__((always_inline)) {
     if (loader) {  // this step's chunk has landed; the next R - 2 may be pending
       if (gp + kGroups * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
       else wait_vm<0>();
@@ -953,9 +1046,42 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
       chunk_pages(pages_addr, cn, pa, pb);
       issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, lane);
     }
-    if (active && ck < nch)
-      compute_chunk<D>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1, L, q,
-                       W, A.scale_log2, lane);
+  };
+  if constexpr (!FP8) {
+    for (int k = 0; k < nst; ++k) {
+      const int ck = gp + kGroups * k;
+      step_begin(k);
+      if (active && ck < nch)
+        compute_chunk<D>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1, L,
+                         q, W, A.scale_log2, lane);
+    }
+  } else {
+    // The inner loop runs chunks whose rows keep their softmax reference;
+    // a chunk that must move it leaves the loop, is finished after the
+    // rescale, and the loop resumes at the next step. (With the rescale
+    // inside the loop the compiler moves the accumulators between
+    // registers on every chunk.)
+    Fp8Chunk<D> X;
+    int k = 0;
+    for (;;) {
+      bool moved = false;
+      for (; k < nst; ++k) {
+        const int ck = gp + kGroups * k;
+        step_begin(k);
+        if (active && ck < nch) {
+          if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
+                              tv1, L, q, W, A.scale_log2, lane, sm.qbuf + r * 8192)) {
+            moved = true;
+            break;
+          }
+          chunk_finish<D>(S, X, tv0, tv1, A.scale_log2, lane);
+        }
+      }
+      if (!moved) break;
+      rescale(S, X.mx);
+      chunk_finish<D>(S, X, tv0, tv1, A.scale_log2, lane);
+      ++k;
+    }
   }
 
   // ---- Merge the groups: group 1's waves hand (m, l, O) of their tile to
