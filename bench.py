@@ -247,7 +247,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the FP8, long-context and mixed workloads")
     ap.add_argument("--only", type=int, default=None,
-                    help="time just this workload (2..5) and print its figures")
+                    help="time just this workload (2..6) and print its figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
