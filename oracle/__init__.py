@@ -92,6 +92,8 @@ class Oracle:
         lib.pa_oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.pa_oracle_kv_append.argtypes = [i32, i32, i32, P, P, P, P, P, i32, i32, i32, P, P, P, P]
         lib.pa_oracle_kv_append.restype = i32
+        lib.pa_oracle_greedy_verdict.argtypes = [i32, P, i32, ctypes.c_int64, P, i32, P, P, P, P]
+        lib.pa_oracle_greedy_verdict.restype = i32
         self.lib = lib
 
     def e4m3_to_double(self, code: int) -> float:
@@ -160,6 +162,32 @@ class Oracle:
             _ptr(v_scales) if kv_fp8 else None)
         if rc != 0:
             raise ValueError(f"oracle rejected its arguments (code {rc})")
+
+    def greedy_verdict_arrays(self, *, q_lens, logits, input_ids, out_ids=None, accepted=None,
+                              next_ids=None):
+        """Greedy verify verdict on host arrays. logits: [T][V] float32, or
+        uint16 bf16 bits. Returns (out_ids [T], accepted [B], next_ids [B])
+        int32; entries of padded slots keep the values of the arrays passed
+        in (default -7)."""
+        ql = _np(q_lens, np.int32)
+        lg = np.ascontiguousarray(logits)
+        if lg.dtype == np.float32:
+            bf = 0
+        elif lg.dtype == np.uint16:
+            bf = 1
+        else:
+            raise ValueError("logits must be float32 or uint16 bf16 bits")
+        T, V = lg.shape
+        ids = _np(input_ids, np.int32)
+        B = int(ql.shape[0])
+        out = np.full(T, -7, np.int32) if out_ids is None else out_ids
+        acc = np.full(B, -7, np.int32) if accepted is None else accepted
+        nxt = np.full(B, -7, np.int32) if next_ids is None else next_ids
+        rc = self.lib.pa_oracle_greedy_verdict(B, _ptr(ql), V, V, _ptr(lg), bf, _ptr(ids),
+                                               _ptr(out), _ptr(acc), _ptr(nxt))
+        if rc != 0:
+            raise ValueError(f"oracle rejected its arguments (code {rc})")
+        return out, acc, nxt
 
     def verify(self, wl, unit_mask=None, threads: Optional[int] = None):
         """Oracle output for a ``workloads.Workload`` whose tensors are on the CPU."""

@@ -378,3 +378,66 @@ int pa_oracle_kv_append(int B, int Hkv, int D, const int32_t *ctx_lens, const in
   free(codes);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Greedy verify verdict.
+ *
+ * Sources: ATOM #3091 ("High-interactivity monokernel decode for
+ * DeepSeek-V4.1-Flash on MI355X"): the verify head gives a step's output ids
+ * and its verdict in one launch, greedy rows included (Engine hooks), and
+ * the next step takes each request's next id from the output ids at the
+ * verdict's accepted count (the review rounds on the head-served verify).
+ *
+ * For sequence b with q = q_b verify rows at t_b .. t_b + q - 1 (q = k + 1:
+ * row 0's input is the last committed token, rows 1..k hold the k draft
+ * tokens, so draft j is input_ids[t_b + 1 + j]):
+ *   a_i      = argmax_v logits[t_b + i][v]      for every row i
+ *   n        = the number of leading drafts the target agrees with:
+ *              the largest n in [0, k] with input_ids[t_b + 1 + j] == a_j
+ *              for all j < n
+ *   out_ids[t_b + i] = a_i,  accepted[b] = n,  next_ids[b] = a_n
+ * (the step emits a_0 .. a_n, the n accepted drafts and one target token).
+ * A padded slot (q = 0) writes nothing.
+ * Readings: argmax takes the lowest index among equal maxima; a NaN never
+ * wins (it compares false); a row with no value above -inf gives index 0.
+ * bf16 logits widen exactly.
+ */
+static double logit_at(const void *logits, int is_bf16, int64_t idx) {
+  if (is_bf16) return pa_oracle_bf16_to_double(((const uint16_t *)logits)[idx]);
+  return (double)((const float *)logits)[idx];
+}
+
+/* Returns 0, or -1 on arguments that cannot describe a call (nothing is
+ * written then). */
+int pa_oracle_greedy_verdict(int B, const int32_t *q_lens, int vocab, int64_t row_stride,
+                             const void *logits, int logits_bf16, const int32_t *input_ids,
+                             int32_t *out_ids, int32_t *accepted, int32_t *next_ids) {
+  if (B < 1 || vocab < 1 || row_stride < vocab || !q_lens || !logits || !input_ids ||
+      !out_ids || !accepted || !next_ids)
+    return -1;
+  for (int b = 0; b < B; ++b)
+    if (q_lens[b] < 0) return -1;
+  int64_t t = 0;
+  for (int b = 0; b < B; ++b) {
+    const int q = q_lens[b];
+    if (q == 0) continue;
+    for (int i = 0; i < q; ++i) {
+      double best = -INFINITY;
+      int arg = 0;
+      for (int v = 0; v < vocab; ++v) {
+        const double x = logit_at(logits, logits_bf16, (t + i) * row_stride + v);
+        if (x > best) {
+          best = x;
+          arg = v;
+        }
+      }
+      out_ids[t + i] = arg;
+    }
+    int n = 0;
+    while (n < q - 1 && input_ids[t + 1 + n] == out_ids[t + n]) ++n;
+    accepted[b] = n;
+    next_ids[b] = out_ids[t + n];
+    t += q;
+  }
+  return 0;
+}

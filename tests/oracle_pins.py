@@ -16,7 +16,12 @@ fixes. The pages print no worked attention values, so the pins are:
 * structural identities: verify row i equals decode at context L - q + i + 1;
   GQA equals MHA with the KV heads repeated;
 * the FP8 e4m3 code table and bf16 widening against torch's own conversions;
-* FP8 attention against dense attention on the dequantised values.
+* FP8 attention against dense attention on the dequantised values;
+* the greedy verify verdict: argmax against numpy's (lowest index among
+  equal maxima), bf16 and fp32 logits agreeing, the acceptance rule on
+  constructed drafts, NaN and tie rows, and the speculative-decoding
+  guarantee that the emitted tokens are the target's own greedy
+  continuation.
 
 ``tests/test_oracle_mutants.py`` plants plausible mistakes into copies of the
 oracle and checks that at least one pin fails for each.
@@ -622,7 +627,144 @@ def pin_append_then_attend(orc):
         t += ql[b]
 
 
+# --------------------------------------------------------------------------
+# Greedy verify verdict.
+# --------------------------------------------------------------------------
+
+def pin_verdict_argmax_matches_numpy(orc):
+    """Per-row argmax equals numpy's (first index of the maximum), with
+    planted exact ties; bf16 logits give the same ids as the same values in
+    float32."""
+    rng = np.random.default_rng(41)
+    q = [6, 1, 8, 3, 6]
+    T, V = sum(q), 1000
+    lg = rng.standard_normal((T, V)).astype(np.float32)
+    for t in range(0, T, 3):  # ties: the maximum appears twice
+        j = int(np.argmax(lg[t]))
+        k = (j + 1 + int(rng.integers(0, V - 1))) % V
+        lg[t, k] = lg[t, j]
+    ids = rng.integers(0, V, T).astype(np.int32)
+    out, acc, nxt = orc.greedy_verdict_arrays(q_lens=q, logits=lg, input_ids=ids)
+    assert np.array_equal(out, np.argmax(lg, axis=1).astype(np.int32))
+    lb = torch.from_numpy(lg).to(torch.bfloat16)
+    out_b, acc_b, nxt_b = orc.greedy_verdict_arrays(q_lens=q, logits=bits(lb), input_ids=ids)
+    out_f, acc_f, nxt_f = orc.greedy_verdict_arrays(q_lens=q, logits=lb.float().numpy(),
+                                                   input_ids=ids)
+    assert np.array_equal(out_b, out_f) and np.array_equal(acc_b, acc_f)
+    assert np.array_equal(out_b, np.argmax(lb.float().numpy(), axis=1).astype(np.int32))
+
+
+def pin_verdict_accept_rule(orc):
+    """Constructed drafts: all accepted, none, a mismatch at j (later matches
+    do not count), q = 1 (nothing to accept), a padded slot (nothing
+    written); row 0's input never matters."""
+    V = 50
+    q = [6, 6, 6, 6, 1, 0, 8]
+    T = sum(q)
+    rng = np.random.default_rng(43)
+    target = rng.integers(0, V, T)
+    lg = rng.standard_normal((T, V)).astype(np.float32) - 10.0
+    lg[np.arange(T), target] = 5.0  # row t's argmax is target[t]
+    ids = np.zeros(T, np.int32)
+    want_n = []
+    t = 0
+    for b, qb in enumerate(q):
+        if qb == 0:
+            want_n.append(None)
+            continue
+        a = target[t:t + qb]
+        d = a[:qb - 1].copy()  # drafts equal to the target's picks
+        n = qb - 1
+        if b == 1:
+            d[0] = (a[0] + 1) % V; n = 0              # first draft wrong
+        if b == 2:
+            d[3] = (a[3] + 2) % V; n = 3              # mismatch at j = 3, later ones match
+        if b == 3:
+            d[2] = (a[2] + 1) % V; d[4] = (a[4] + 1) % V; n = 2
+        if b == 4:
+            n = 0
+        ids[t] = rng.integers(0, V)
+        ids[t + 1:t + qb] = d
+        want_n.append(n)
+        t += qb
+    out, acc, nxt = orc.greedy_verdict_arrays(q_lens=q, logits=lg, input_ids=ids)
+    assert np.array_equal(out, target.astype(np.int32))
+    t = 0
+    for b, qb in enumerate(q):
+        if qb == 0:
+            assert acc[b] == -7 and nxt[b] == -7  # untouched
+            continue
+        assert acc[b] == want_n[b], (b, acc[b], want_n[b])
+        assert nxt[b] == target[t + want_n[b]]
+        t += qb
+    ids2 = ids.copy()
+    t = 0
+    for qb in q:  # a different last-committed token changes nothing
+        if qb:
+            ids2[t] = (ids2[t] + 7) % V
+        t += qb
+    _, acc2, nxt2 = orc.greedy_verdict_arrays(q_lens=q, logits=lg, input_ids=ids2)
+    assert np.array_equal(acc2, acc) and np.array_equal(nxt2, nxt)
+
+
+def pin_verdict_nan_and_ties(orc):
+    """A NaN never wins; equal maxima give the lowest index; a row with no
+    value above -inf gives 0."""
+    inf, nan = np.inf, np.nan
+    rows = np.array([
+        [nan, 1.0, 3.0, 3.0, 2.0],
+        [-inf, -inf, -inf, -inf, -inf],
+        [-inf, nan, nan, -inf, nan],
+        [0.5, 0.5, 0.5, 0.5, 0.5],
+        [1.0, nan, inf, nan, inf],
+    ], dtype=np.float32)
+    out, _, _ = orc.greedy_verdict_arrays(q_lens=[5], logits=rows, input_ids=np.zeros(5))
+    assert out.tolist() == [2, 0, 0, 0, 2]
+
+
+def pin_verdict_is_greedy_continuation(orc):
+    """The speculative-decoding guarantee: the emitted tokens a_0 .. a_n are
+    exactly what the target produces greedily one token at a time from the
+    committed prefix (a toy target whose logits depend on the whole prefix,
+    drafts from a toy draft model that agrees most of the time)."""
+    V = 97
+
+    def target_logits(prefix):
+        r = np.random.default_rng(hash(tuple(prefix)) % (1 << 32))
+        return r.standard_normal(V).astype(np.float32)
+
+    rng = np.random.default_rng(47)
+    for trial in range(40):
+        k = int(rng.integers(0, 8))
+        prefix = [int(x) for x in rng.integers(0, V, int(rng.integers(1, 6)))]
+        drafts, ctx = [], list(prefix)
+        for _ in range(k):  # a draft model that agrees with the target 80% of the time
+            g = int(np.argmax(target_logits(ctx)))
+            d = g if rng.random() < 0.8 else int(rng.integers(0, V))
+            drafts.append(d)
+            ctx.append(d)
+        rows = [target_logits(prefix + drafts[:i]) for i in range(k + 1)]
+        ids = [prefix[-1]] + drafts
+        out, acc, nxt = orc.greedy_verdict_arrays(q_lens=[k + 1], logits=np.stack(rows),
+                                                  input_ids=ids)
+        n = int(acc[0])
+        emitted = [int(x) for x in out[:n + 1]]
+        greedy, ctx = [], list(prefix)
+        for _ in range(n + 1):
+            g = int(np.argmax(target_logits(ctx)))
+            greedy.append(g)
+            ctx.append(g)
+        assert emitted == greedy, (trial, emitted, greedy)
+        assert int(nxt[0]) == greedy[-1]
+        assert emitted[:n] == drafts[:n]
+        assert n == k or drafts[n] != greedy[n]
+
+
 ALL_PINS = [
+    pin_verdict_argmax_matches_numpy,
+    pin_verdict_accept_rule,
+    pin_verdict_nan_and_ties,
+    pin_verdict_is_greedy_continuation,
     pin_e4m3_encode_matches_torch,
     pin_e4m3_encode_nearest,
     pin_kv_append_fp8,

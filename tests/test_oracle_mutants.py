@@ -67,6 +67,20 @@ MUTANTS = {
     "encode_no_sign": ("(signbit(v) ? 0x80 : 0)", "0"),
     # append: V rows taken from the new K
     "append_v_from_k": ("const uint16_t *vr = v_new + ", "const uint16_t *vr = k_new + "),
+    # verdict: a draft compared with the argmax of its own row
+    "verdict_alignment": ("input_ids[t + 1 + n] == out_ids[t + n]", "input_ids[t + 1 + n] == out_ids[t + 1 + n]"),
+    # verdict: ties go to the highest index
+    "verdict_ties_high": ("        if (x > best) {\n          best = x;\n          arg = v;",
+                          "        if (x >= best) {\n          best = x;\n          arg = v;"),
+    # verdict: NaN wins
+    "verdict_nan_wins": ("        if (x > best) {\n          best = x;\n          arg = v;",
+                         "        if (!(x <= best)) {\n          best = x;\n          arg = v;"),
+    # verdict: the next id is the last accepted draft instead of the target's token after it
+    "verdict_next_off": ("next_ids[b] = out_ids[t + n];", "next_ids[b] = out_ids[t + (n > 0 ? n - 1 : 0)];"),
+    # verdict: every matching draft counts, not only the leading run
+    "verdict_all_matches": ("while (n < q - 1 && input_ids[t + 1 + n] == out_ids[t + n]) ++n;",
+                            "for (int j = 0; j < q - 1; ++j) n += (input_ids[t + 1 + j] == out_ids[t + j]);"),
+
 }
 
 
