@@ -211,6 +211,49 @@ def measure_append(wl, steps: int, warmup: int):
             "timed_as": "hip-graph replay"}
 
 
+def measure_verdict(q_lens, vocab: int, steps: int, warmup: int):
+    """Time pa_verify_greedy over synthetic bf16 logits [T][vocab] (one call
+    per step, `steps` calls in one replayed HIP graph). Returns the time per
+    call and the logits bytes a call reads."""
+    import torch
+
+    import paged_kv_cache_verify_amd as pav
+
+    B, T = len(q_lens), sum(q_lens)
+    shape = pav.make_shape(num_seqs=B, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                           num_blocks=4 * B, max_blocks_per_seq=4, softmax_scale=0.125)
+    plan = pav.pa_plan(shape, [max(q, 1) for q in q_lens], q_lens, None, device=0)
+    gen = torch.Generator().manual_seed(77)
+    logits = torch.randn((T, vocab), generator=gen).to(torch.bfloat16).to("cuda:0")
+    ids = torch.randint(0, vocab, (T,), generator=gen, dtype=torch.int32).to("cuda:0")
+    out = torch.empty((T,), dtype=torch.int32, device="cuda:0")
+    acc = torch.empty((B,), dtype=torch.int32, device="cuda:0")
+    nxt = torch.empty((B,), dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            pav.pa_verify_greedy(plan, logits, ids, out, acc, nxt, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(steps):
+            pav.pa_verify_greedy(plan, logits, ids, out, acc, nxt, s)
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        g.replay()
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - w0) / steps
+    del g
+    pav.pa_free(plan)
+    nbytes = T * vocab * 2
+    return {"us_per_call": round(us, 2), "logits_bytes_per_call": nbytes,
+            "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "rows": T, "vocab": vocab,
+            "timed_as": "hip-graph replay (logits resident in the Infinity Cache)"}
+
+
 def cpu_baseline(wl, budget_s: float = 10.0):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -384,6 +427,10 @@ def main():
             }
             del wlb
         del wl6
+        rv = measure_verdict([6] * 8, 131072, max(50, args.steps), max(5, args.warmup // 4))
+        log(f"greedy verdict, 8 x 6 verify rows over a 131,072-entry vocabulary (bf16 logits): "
+            f"{rv['us_per_call']} us/call = {rv['GB_s']} GB/s")
+        extra["greedy verdict, 8 sequences x 6 rows, vocab 131072, bf16 logits"] = rv
         ra = measure_append(wl, max(50, args.steps), max(5, args.warmup // 4))
         log(f"kv append of workload {main_cfg}'s {ra['new_tokens']} new tokens (bf16): "
             f"{ra['us_per_call']} us/call = {ra['GB_s']} GB/s")

@@ -174,6 +174,36 @@ pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_n
                        const int32_t* block_table, void* k_pool, void* v_pool,
                        float* k_scales, float* v_scales, void* stream);
 
+/*
+ * Greedy verify verdict: the step after the target's head in a verify round.
+ * Source: ATOM #3091 ("High-interactivity monokernel decode for
+ * DeepSeek-V4.1-Flash on MI355X"): the verify head gives a step's ids and
+ * verdict in one launch for greedy rows (Engine hooks), and the next step's
+ * input is each request's output id at the verdict's accepted count (the
+ * review rounds on the head-served verify).
+ * For sequence b with q = q_b verify rows t_b .. t_b + q - 1 (row 0's input
+ * is the last committed token, rows 1..q-1 hold the q - 1 draft tokens):
+ *   a_i = argmax over v < vocab of logits[t_b + i][v]   (lowest index among
+ *         equal maxima; a NaN never wins; no value above -inf gives 0)
+ *   n   = the largest n <= q - 1 with input_ids[t_b + 1 + j] == a_j for all
+ *         j < n (the leading drafts the target agrees with)
+ *   out_ids[t_b + i] = a_i, accepted[b] = n, next_ids[b] = a_n
+ * The step emits a_0 .. a_n. A padded slot (q = 0) writes nothing.
+ *   logits     [T][row_stride] bf16 or fp32 (logits_dtype), 16-byte aligned,
+ *              row_stride >= vocab with a row spanning a multiple of 16 bytes
+ *   input_ids  [T] int32, the verify rows' input tokens (layout of q's rows)
+ *   out_ids    [T] int32; accepted, next_ids [B] int32
+ * Uses the plan's query lengths and its scratch (argmax partials); enqueued
+ * on `stream`, allocation-free and graph-capturable. Returns PA_E_INVALID
+ * for a missing pointer, vocab < 1, a bad stride or alignment, or a
+ * host-only plan, PA_E_UNSUPPORTED for another logits dtype, PA_E_HIP if a
+ * launch fails.
+ */
+pa_status pa_verify_greedy(const pa_plan_t* plan, const void* logits, pa_dtype logits_dtype,
+                           int32_t vocab, int64_t row_stride, const int32_t* input_ids,
+                           int32_t* out_ids, int32_t* accepted, int32_t* next_ids,
+                           void* stream);
+
 /* Release a plan and its device memory. NULL-safe. The caller makes sure no
  * call that uses the plan is still in flight. */
 void pa_free(pa_plan_t* plan);

@@ -1,8 +1,8 @@
 """Paged verify attention for MI355X: a thin binding over libpa_verify.so.
 
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
-pa_kv_append, pa_free, pa_last_error, pa_plan_info, pa_plan_items,
-pa_set_partition_events). This module only marshals arguments: torch tensors
+pa_kv_append, pa_verify_greedy, pa_free, pa_last_error, pa_plan_info,
+pa_plan_items, pa_set_partition_events). This module only marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
 there is no other path, and loading fails loudly if the library is missing.
@@ -21,8 +21,8 @@ PA_OK, PA_E_INVALID, PA_E_UNSUPPORTED, PA_E_HIP, PA_E_NOMEM = 0, 1, 2, 3, 4
 PA_BF16, PA_FP8_E4M3, PA_FP32 = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
-EXPORTED = ("pa_plan", "pa_decode_verify", "pa_kv_append", "pa_free", "pa_last_error",
-            "pa_plan_info", "pa_plan_items", "pa_set_partition_events")
+EXPORTED = ("pa_plan", "pa_decode_verify", "pa_kv_append", "pa_verify_greedy", "pa_free",
+            "pa_last_error", "pa_plan_info", "pa_plan_items", "pa_set_partition_events")
 
 
 class PaShape(ctypes.Structure):
@@ -68,6 +68,9 @@ def library() -> ctypes.CDLL:
         lib.pa_decode_verify.restype = ctypes.c_int
         lib.pa_kv_append.argtypes = [P, P, P, P, P, P, P, P, P]
         lib.pa_kv_append.restype = ctypes.c_int
+        lib.pa_verify_greedy.argtypes = [P, P, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, P,
+                                         P, P, P, P]
+        lib.pa_verify_greedy.restype = ctypes.c_int
         lib.pa_free.argtypes = [P]
         lib.pa_free.restype = None
         lib.pa_last_error.argtypes = []
@@ -191,6 +194,27 @@ def pa_kv_append(plan: Plan, k_new, v_new, block_table, k_pool, v_pool, k_scales
     _check(library().pa_kv_append(plan.handle, _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                   _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales),
                                   _stream_handle(stream)))
+
+
+def pa_verify_greedy(plan: Plan, logits, input_ids, out_ids, accepted, next_ids,
+                     stream=None) -> None:
+    """Greedy verify verdict (see pa_verify_greedy in include/pa_verify.h):
+    logits [T][V] (bf16 or float32; a row may be a strided view with unit
+    last stride), input_ids [T] int32 -> out_ids [T], accepted [B],
+    next_ids [B] int32."""
+    import torch
+
+    dt = {torch.bfloat16: PA_BF16, torch.float32: PA_FP32}.get(logits.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [T][V] with unit stride along V")
+    if not logits.is_cuda:
+        raise ValueError("the library takes device tensors")
+    _check(library().pa_verify_greedy(plan.handle, ctypes.c_void_p(logits.data_ptr()), dt,
+                                      logits.shape[1], logits.stride(0), _ptr(input_ids),
+                                      _ptr(out_ids), _ptr(accepted), _ptr(next_ids),
+                                      _stream_handle(stream)))
 
 
 def pa_free(plan: Plan) -> None:

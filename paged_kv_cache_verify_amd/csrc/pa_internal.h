@@ -89,6 +89,27 @@ struct AppendArgs {
   int32_t num_blocks;
 };
 
+// The greedy verify verdict.
+constexpr int kVerdictSlices = 32;  // workgroups per verify row in the argmax pass
+struct VerdictArgs {
+  const void* logits;        // [T][row_stride], bf16 or fp32
+  int64_t row_stride;        // elements
+  int32_t vocab;
+  int32_t slice;             // vocabulary entries per slice (a multiple of 8)
+  int32_t logits_bf16;
+  int32_t num_tokens;        // T
+  int32_t num_seqs;          // B
+  const int32_t* seq_rows;   // [B][2]: first verify row, verify rows (q)
+  const int32_t* input_ids;  // [T]
+  float* part_val;           // [T][kVerdictSlices]
+  int32_t* part_idx;         // [T][kVerdictSlices]
+  int32_t* out_ids;          // [T]
+  int32_t* accepted;         // [B]
+  int32_t* next_ids;         // [B]
+};
+
+hipError_t launch_verdict(const VerdictArgs& a, hipStream_t stream);
+
 // ntmax: row tiles of 16 the kernel is built for (ceil(max q x G / 16));
 // items with fewer rows skip the missing tiles. One workgroup per CU.
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,

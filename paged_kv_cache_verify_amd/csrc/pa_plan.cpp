@@ -54,8 +54,12 @@ struct pa_plan_s {
   std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
   int32_t max_parts = 0;        // most partials of any split pair
   std::vector<int32_t> tokens;  // [T][2]: sequence, position of each new token
+  std::vector<int32_t> seq_rows;  // [B][2]: first verify row, verify rows (q)
   WorkItem* d_items = nullptr;
   int32_t* d_tokens = nullptr;
+  int32_t* d_seq_rows = nullptr;
+  float* d_verdict_val = nullptr;  // [T][kVerdictSlices] argmax partials
+  int32_t* d_verdict_idx = nullptr;
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
   float* d_part_ml = nullptr;
@@ -92,8 +96,14 @@ void release_device(pa_plan_s* p) {
   if (p->d_part_o) (void)hipFree(p->d_part_o);
   if (p->d_part_ml) (void)hipFree(p->d_part_ml);
   if (p->d_tokens) (void)hipFree(p->d_tokens);
+  if (p->d_seq_rows) (void)hipFree(p->d_seq_rows);
+  if (p->d_verdict_val) (void)hipFree(p->d_verdict_val);
+  if (p->d_verdict_idx) (void)hipFree(p->d_verdict_idx);
   p->d_items = nullptr;
   p->d_tokens = nullptr;
+  p->d_seq_rows = nullptr;
+  p->d_verdict_val = nullptr;
+  p->d_verdict_idx = nullptr;
   p->d_red = nullptr;
   p->d_part_o = nullptr;
   p->d_part_ml = nullptr;
@@ -256,6 +266,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       si.n_parts = 0;
       si.piece = 0;
       si.slot_base = -1;
+      p->seq_rows.push_back(q_off);
+      p->seq_rows.push_back(si.q_len);
       q_off += si.q_len;
       for (int i = 0; i < si.q_len; ++i) {
         p->tokens.push_back(b);
@@ -375,6 +387,13 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     e = upload((void**)&p->d_red, p->red.data(), p->red.size() * sizeof(ReduceItem));
   if (e == hipSuccess)
     e = upload((void**)&p->d_tokens, p->tokens.data(), p->tokens.size() * sizeof(int32_t));
+  if (e == hipSuccess)
+    e = upload((void**)&p->d_seq_rows, p->seq_rows.data(), p->seq_rows.size() * sizeof(int32_t));
+  const size_t n_verdict = p->tokens.size() / 2 * kVerdictSlices;
+  if (e == hipSuccess && n_verdict > 0) {
+    e = hipMalloc((void**)&p->d_verdict_val, n_verdict * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_verdict_idx, n_verdict * sizeof(int32_t));
+  }
   if (e == hipSuccess && p->n_slots > 0) {
     e = hipMalloc((void**)&p->d_part_o,
                   (size_t)p->n_slots * p->rows_stride * s.head_dim * sizeof(float));
@@ -477,6 +496,48 @@ pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_n
   a.num_blocks = s.num_blocks;
   hipError_t e = launch_append(a, s.head_dim, fp8, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_verify_greedy(const pa_plan_t* plan, const void* logits, pa_dtype logits_dtype,
+                           int32_t vocab, int64_t row_stride, const int32_t* input_ids,
+                           int32_t* out_ids, int32_t* accepted, int32_t* next_ids, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+  if (logits_dtype != PA_BF16 && logits_dtype != PA_FP32)
+    return fail(PA_E_UNSUPPORTED, "logits must be bf16 or fp32");
+  if (vocab < 1) return fail(PA_E_INVALID, "vocab %d < 1", vocab);
+  if (row_stride < vocab)
+    return fail(PA_E_INVALID, "row_stride %lld is smaller than vocab %d", (long long)row_stride,
+                vocab);
+  const int esz = logits_dtype == PA_BF16 ? 2 : 4;
+  if ((row_stride * esz) % 16 != 0)
+    return fail(PA_E_INVALID, "a logits row must span a multiple of 16 bytes (row_stride %lld)",
+                (long long)row_stride);
+  if (plan->tokens.empty()) return PA_OK;  // every sequence is a padded slot
+  if (!logits || !input_ids || !out_ids || !accepted || !next_ids)
+    return fail(PA_E_INVALID, "logits, input_ids, out_ids, accepted and next_ids are required");
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+    return fail(PA_E_INVALID, "logits must be 16-byte aligned");
+
+  VerdictArgs a{};
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = vocab;
+  const int64_t per = ((int64_t)vocab + kVerdictSlices - 1) / kVerdictSlices;
+  a.slice = (int32_t)(((per + 7) / 8) * 8);
+  a.logits_bf16 = logits_dtype == PA_BF16;
+  a.num_tokens = (int32_t)(plan->tokens.size() / 2);
+  a.num_seqs = plan->shape.num_seqs;
+  a.seq_rows = plan->d_seq_rows;
+  a.input_ids = input_ids;
+  a.part_val = plan->d_verdict_val;
+  a.part_idx = plan->d_verdict_idx;
+  a.out_ids = out_ids;
+  a.accepted = accepted;
+  a.next_ids = next_ids;
+  hipError_t e = launch_verdict(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "verdict kernel launch");
   return PA_OK;
 }
 

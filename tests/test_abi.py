@@ -110,6 +110,8 @@ def test_null_arguments_are_refused():
                                 None) == pav.PA_E_INVALID
     assert lib.pa_kv_append(None, None, None, None, None, None, None, None,
                             None) == pav.PA_E_INVALID
+    assert lib.pa_verify_greedy(None, None, pav.PA_BF16, 8, 8, None, None, None, None,
+                                None) == pav.PA_E_INVALID
     lib.pa_free(None)  # NULL-safe
 
 
@@ -121,6 +123,8 @@ def test_host_only_plan_refuses_to_run():
         pav._check(st)
     assert e.value.status == pav.PA_E_INVALID
     st = pav.library().pa_kv_append(plan.handle, 4, 4, 4, 4, 4, None, None, None)
+    assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
+    st = pav.library().pa_verify_greedy(plan.handle, 16, pav.PA_BF16, 8, 8, 4, 4, 4, 4, None)
     assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
     plan.close()
 
