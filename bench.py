@@ -63,7 +63,7 @@ def load_traffic(workload_key: str):
     return rec.get("bytes_per_launch")
 
 
-def measure(wl, steps: int, warmup: int, partition_tokens=None):
+def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None):
     """Time `steps` calls on rotating pool copies; returns a dict of figures.
 
     The timed region is one replay of a HIP graph holding the `steps` calls
@@ -78,9 +78,26 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None):
     import paged_kv_cache_verify_amd as pav
 
     dev = wl.to("cuda:0")
-    plan = pav.plan_for(dev, device=0, partition_tokens=partition_tokens)
-    info = plan.info()
-    kv = info["kv_bytes"]
+    lens_dev = None
+    if bound_extra is None:
+        plan = pav.plan_for(dev, device=0, partition_tokens=partition_tokens)
+        info = plan.info()
+        kv = info["kv_bytes"]
+    else:
+        # A plan on upper bounds (every length + bound_extra) and calls that
+        # read the actual lengths from device memory.
+        shape = pav.make_shape(
+            num_seqs=wl.num_seqs, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+            head_dim=wl.head_dim, num_blocks=wl.num_blocks,
+            max_blocks_per_seq=wl.max_blocks_per_seq, kv_dtype=wl.kv_dtype,
+            out_dtype=wl.out_dtype, softmax_scale=wl.softmax_scale, sinks_mode=wl.sinks_mode,
+            partition_tokens=partition_tokens or 0, lengths_are_bounds=1)
+        win = None if wl.window is None else wl.window.tolist()
+        plan = pav.pa_plan(shape, (wl.ctx_lens + bound_extra).tolist(), wl.q_lens.tolist(), win,
+                           device=0)
+        info = plan.info()
+        kv = wl.kv_bytes()  # the bytes the actual lengths make visible
+        lens_dev = wl.ctx_lens.to("cuda:0")
     copies = 1 if kv >= (1 << 30) else int(math.ceil((1 << 30) / kv)) + 1
     pools = [(dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales)]
     for _ in range(copies - 1):
@@ -91,7 +108,11 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None):
 
     def call(i):
         kp, vp, ks, vs = pools[i % copies]
-        pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out, s)
+        if lens_dev is None:
+            pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out, s)
+        else:
+            pav.pa_decode_verify_dev(plan, lens_dev, dev.q, kp, vp, dev.block_table, ks, vs,
+                                     dev.sinks, out, s)
 
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -427,6 +448,20 @@ def main():
             }
             del wlb
         del wl6
+        # The headline workload through the device-length call: a plan built
+        # on bounds 64 tokens past every length, the lengths read at run time.
+        wlb = workloads.make(main_cfg, extra_max_blocks=5)
+        rb = measure(wlb, max(20, args.steps // 4), max(5, args.warmup // 4), bound_extra=64)
+        msb = rb["wall_ms_per_step"]
+        log(f"workload {main_cfg}, lengths read on the device (plan on bounds +64): "
+            f"{1e3 * msb:.1f} us/call; partition kernel {1e3 * rb['partition_ms_mean']:.1f} us")
+        extra[f"workload {main_cfg}, lengths read on the device (plan on bounds L + 64)"] = {
+            "us_per_call": round(1e3 * msb, 2),
+            "GB_s": round(rb["kv_bytes"] / (msb * 1e-3) / 1e9, 1),
+            "partition_kernel_us": round(1e3 * rb["partition_ms_mean"], 2),
+            "work_items": rb["plan"]["work_items"],
+        }
+        del wlb
         rv = measure_verdict([6] * 8, 131072, max(50, args.steps), max(5, args.warmup // 4))
         log(f"greedy verdict, 8 x 6 verify rows over a 131,072-entry vocabulary (bf16 logits): "
             f"{rv['us_per_call']} us/call = {rv['GB_s']} GB/s")

@@ -102,6 +102,13 @@ typedef struct {
                                  multiple of 16 up to PA_MAX_ITEM_KEYS, or 0
                                  to let the plan choose */
   int32_t sinks_mode;         /* 0 none, 1 sinks[Hq], 2 sinks[B][Hq] */
+  int32_t lengths_are_bounds; /* 0: context_lens are the lengths; 1: they
+                                 are per-sequence upper bounds for calls
+                                 that read the lengths from device memory
+                                 (pa_decode_verify_dev); the work items
+                                 then cover every key a length up to the
+                                 bound can make visible (a windowed
+                                 sequence from key 0) */
 } pa_shape;
 
 /*
@@ -143,6 +150,29 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q,
                            const int32_t* block_table, const float* k_scales,
                            const float* v_scales, const float* sinks, void* out,
                            void* stream);
+
+/*
+ * pa_decode_verify with the context lengths read from device memory at run
+ * time, so that one captured graph serves every step of a decode loop while
+ * the lengths advance on the device. Source: ATOM #3091 ("High-interactivity
+ * monokernel decode for DeepSeek-V4.1-Flash on MI355X", Summary: the next
+ * step is laid out from the device-resident verdict; How to reproduce: full
+ * graph capture); ATOM #2843 (Motivation: plans built on upper bounds,
+ * scratch sized by the largest query).
+ *   context_lens_dev  device [B] int32: L_b for this call. The plan's
+ *                     context_lens are upper bounds; the kernels clamp L_b
+ *                     to [q_b, bound_b]. Query lengths, windows and sinks
+ *                     are the plan's.
+ * The block table must hold valid page ids for the first ceil(L_b / 16)
+ * entries of each row (entries past the length are not read). A plan with
+ * windows must have been built with lengths_are_bounds = 1 (PA_E_INVALID
+ * otherwise). Everything else as pa_decode_verify.
+ */
+pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_lens_dev,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const float* k_scales,
+                               const float* v_scales, const float* sinks, void* out,
+                               void* stream);
 
 /*
  * Paged KV append: write the plan's new tokens (the last q_b positions of

@@ -1,7 +1,7 @@
 """Paged verify attention for MI355X: a thin binding over libpa_verify.so.
 
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
-pa_kv_append, pa_verify_greedy, pa_free, pa_last_error, pa_plan_info,
+pa_decode_verify_dev, pa_kv_append, pa_verify_greedy, pa_free, pa_last_error, pa_plan_info,
 pa_plan_items, pa_set_partition_events). This module only marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
@@ -21,8 +21,9 @@ PA_OK, PA_E_INVALID, PA_E_UNSUPPORTED, PA_E_HIP, PA_E_NOMEM = 0, 1, 2, 3, 4
 PA_BF16, PA_FP8_E4M3, PA_FP32 = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
-EXPORTED = ("pa_plan", "pa_decode_verify", "pa_kv_append", "pa_verify_greedy", "pa_free",
-            "pa_last_error", "pa_plan_info", "pa_plan_items", "pa_set_partition_events")
+EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_kv_append",
+            "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info", "pa_plan_items",
+            "pa_set_partition_events")
 
 
 class PaShape(ctypes.Structure):
@@ -40,6 +41,7 @@ class PaShape(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("partition_tokens", ctypes.c_int32),
         ("sinks_mode", ctypes.c_int32),
+        ("lengths_are_bounds", ctypes.c_int32),
     ]
 
 
@@ -66,6 +68,8 @@ def library() -> ctypes.CDLL:
         lib.pa_plan.restype = ctypes.c_int
         lib.pa_decode_verify.argtypes = [P, P, P, P, P, P, P, P, P, P]
         lib.pa_decode_verify.restype = ctypes.c_int
+        lib.pa_decode_verify_dev.argtypes = [P, P, P, P, P, P, P, P, P, P, P]
+        lib.pa_decode_verify_dev.restype = ctypes.c_int
         lib.pa_kv_append.argtypes = [P, P, P, P, P, P, P, P, P]
         lib.pa_kv_append.restype = ctypes.c_int
         lib.pa_verify_greedy.argtypes = [P, P, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, P,
@@ -104,11 +108,12 @@ def _i32_array(vals: Optional[Sequence[int]]):
 
 def make_shape(*, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
                max_blocks_per_seq, kv_dtype="bf16", out_dtype="bf16", softmax_scale,
-               partition_tokens=0, sinks_mode=0, block_size=16, q_dtype="bf16") -> PaShape:
+               partition_tokens=0, sinks_mode=0, block_size=16, q_dtype="bf16",
+               lengths_are_bounds=0) -> PaShape:
     dt = {"bf16": PA_BF16, "fp8": PA_FP8_E4M3, "fp32": PA_FP32}
     return PaShape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                    max_blocks_per_seq, dt[q_dtype], dt[kv_dtype], dt[out_dtype],
-                   float(softmax_scale), partition_tokens, sinks_mode)
+                   float(softmax_scale), partition_tokens, sinks_mode, lengths_are_bounds)
 
 
 class Plan:
@@ -184,6 +189,16 @@ def pa_decode_verify(plan: Plan, q, k_pool, v_pool, block_table, k_scales, v_sca
     _check(library().pa_decode_verify(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                       _ptr(block_table), _ptr(k_scales), _ptr(v_scales),
                                       _ptr(sinks), _ptr(out), _stream_handle(stream)))
+
+
+def pa_decode_verify_dev(plan: Plan, context_lens_dev, q, k_pool, v_pool, block_table, k_scales,
+                         v_scales, sinks, out, stream=None) -> None:
+    """pa_decode_verify with the lengths read from a device int32 [B] tensor
+    (the plan's lengths are upper bounds)."""
+    _check(library().pa_decode_verify_dev(plan.handle, _ptr(context_lens_dev), _ptr(q),
+                                          _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                          _ptr(k_scales), _ptr(v_scales), _ptr(sinks), _ptr(out),
+                                          _stream_handle(stream)))
 
 
 def pa_kv_append(plan: Plan, k_new, v_new, block_table, k_pool, v_pool, k_scales=None,

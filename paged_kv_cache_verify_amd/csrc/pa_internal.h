@@ -71,6 +71,9 @@ struct KernelArgs {
   int32_t sinks_mode;
   int32_t out_fp32;
   float scale_log2;  // softmax scale x log2(e)
+  // Device context lengths [B] read at run time (the plan's lengths are
+  // then upper bounds), or null: the plan's own lengths.
+  const int32_t* dev_ctx;
 };
 
 // The new tokens of a verify step, for the paged KV append kernel.

@@ -958,13 +958,24 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
-  const int L = it.ctx_len, q = it.q_len, W = it.window;
+  const int q = it.q_len, W = it.window;
+  int L = it.ctx_len;
+  int tv0 = it.key_begin, tv1 = it.key_end;
+  if (A.dev_ctx) {
+    // Lengths read at run time (the plan was built on upper bounds, which
+    // its items cover): clamp to [q, bound], then clip the item's keys to
+    // what this length makes visible. An item may end up empty.
+    L = min(max(A.dev_ctx[b], q), L);
+    const int lo = W > 0 ? max(0, L - q - W + 1) : 0;
+    tv0 = max(tv0, lo);
+    tv1 = min(tv1, L);
+  }
   const int rows = q * G;
   const int nt = (rows + 15) >> 4;  // row tiles; waves r >= nt do not compute
   const bool active = r < nt;
-  const int tv0 = it.key_begin, tv1 = it.key_end;
   const int tokbase = (tv0 >> 4) << 4;
-  const int nch = (tv1 - tokbase + kChunk - 1) / kChunk;  // <= kMaxItemChunks
+  // <= kMaxItemChunks: [tv0, tv1) lies inside the planned item
+  const int nch = tv1 > tv0 ? (tv1 - tokbase + kChunk - 1) / kChunk : 0;
   const int nst = (nch + kGroups - 1) / kGroups;           // steps: one chunk per group
 
   // Page ids of every chunk (a page past the item's end repeats the

@@ -147,6 +147,8 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
                 s->partition_tokens, kMaxItemKeys);
   if (s->sinks_mode < 0 || s->sinks_mode > 2)
     return fail(PA_E_INVALID, "sinks_mode %d is not 0, 1 or 2", s->sinks_mode);
+  if (s->lengths_are_bounds != 0 && s->lengths_are_bounds != 1)
+    return fail(PA_E_INVALID, "lengths_are_bounds %d is not 0 or 1", s->lengths_are_bounds);
   const int G = s->num_q_heads / s->num_kv_heads;
   int64_t total_q = 0;
   for (int b = 0; b < s->num_seqs; ++b) {
@@ -261,7 +263,9 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       si.q_off = q_off;
       si.window = window ? window[b] : 0;
       si.lo = 0;
-      if (si.q_len > 0 && si.window > 0)
+      // With lengths that are upper bounds, a shorter length moves a window
+      // earlier: the items then cover a windowed sequence from key 0.
+      if (si.q_len > 0 && si.window > 0 && !s.lengths_are_bounds)
         si.lo = std::max(0, si.ctx_len - si.q_len - si.window + 1);
       si.n_parts = 0;
       si.piece = 0;
@@ -410,9 +414,11 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
   return PA_OK;
 }
 
-pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_pool,
-                           const void* v_pool, const int32_t* block_table, const float* k_scales,
-                           const float* v_scales, const float* sinks, void* out, void* stream) {
+namespace {
+
+pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* block_table, const float* k_scales,
+                 const float* v_scales, const float* sinks, void* out, void* stream) {
   if (!plan) return fail(PA_E_INVALID, "plan is NULL");
   if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
   const pa_shape& s = plan->shape;
@@ -449,6 +455,7 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
   a.sinks_mode = s.sinks_mode;
   a.out_fp32 = s.out_dtype == PA_FP32;
   a.scale_log2 = s.softmax_scale * kLog2e;
+  a.dev_ctx = dev_ctx;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -462,6 +469,32 @@ pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_p
   e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, plan->max_parts, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_decode_verify(const pa_plan_t* plan, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_table, const float* k_scales,
+                           const float* v_scales, const float* sinks, void* out, void* stream) {
+  return decode(plan, nullptr, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks, out,
+                stream);
+}
+
+pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_lens_dev,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const float* k_scales,
+                               const float* v_scales, const float* sinks, void* out,
+                               void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (!context_lens_dev) return fail(PA_E_INVALID, "context_lens_dev is required");
+  if (!plan->shape.lengths_are_bounds)
+    for (const SeqInfo& si : plan->seqs)
+      if (si.q_len > 0 && si.window > 0)
+        return fail(PA_E_INVALID,
+                    "a windowed plan read with device lengths must be built with "
+                    "lengths_are_bounds = 1");
+  return decode(plan, context_lens_dev, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
+                out, stream);
 }
 
 pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,

@@ -34,9 +34,23 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(pav.EXPORTED)
 
 
-def test_struct_layout_matches_header():
-    # 13 four-byte fields, no padding: the ctypes mirror must have the same size.
-    assert ctypes.sizeof(pav.PaShape) == 13 * 4
+def test_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of pa_shape has the header's size and field offsets
+    (a C program built from the header prints them)."""
+    import subprocess
+
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in pav.PaShape._fields_]
+    src.write_text(
+        "#include <stddef.h>\n#include <stdio.h>\n#include \"pa_verify.h\"\n"
+        "int main(void) { printf(\"%zu\", sizeof(pa_shape));"
+        + "".join(f' printf(" %zu", offsetof(pa_shape, {f}));' for f in fields)
+        + " return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert got[0] == ctypes.sizeof(pav.PaShape)
+    assert got[1:] == [getattr(pav.PaShape, f).offset for f in fields]
 
 
 def base_shape(**kw):
@@ -64,6 +78,7 @@ REFUSALS = [
     (dict(partition_tokens=100), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
     (dict(partition_tokens=-16), [100, 50], [6, 6], None, pav.PA_E_INVALID, "partition"),
     (dict(sinks_mode=3), [100, 50], [6, 6], None, pav.PA_E_INVALID, "sinks_mode"),
+    (dict(lengths_are_bounds=2), [100, 50], [6, 6], None, pav.PA_E_INVALID, "lengths_are_bounds"),
     (dict(partition_tokens=8192 + 16), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED,
      "work item"),
     ({}, [100, 50], [9, 6], None, pav.PA_E_UNSUPPORTED, "verify limit"),
@@ -112,6 +127,8 @@ def test_null_arguments_are_refused():
                             None) == pav.PA_E_INVALID
     assert lib.pa_verify_greedy(None, None, pav.PA_BF16, 8, 8, None, None, None, None,
                                 None) == pav.PA_E_INVALID
+    assert lib.pa_decode_verify_dev(None, None, None, None, None, None, None, None, None, None,
+                                    None) == pav.PA_E_INVALID
     lib.pa_free(None)  # NULL-safe
 
 
@@ -205,6 +222,22 @@ def test_head256_worklist_at_full_size():
     assert info["kv_bytes"] == 8 * 150000 * (2 * 256 + 8)
     assert info["work_items"] <= 256  # one round of the device's CUs
     plan.close()
+
+
+def test_bounded_plan_covers_windows_from_key_zero():
+    """With lengths_are_bounds a windowed sequence's items start at key 0 (a
+    shorter run-time length moves its window earlier); without it they start
+    at the window of the given length."""
+    ctx, q, win = [5000, 3000], [6, 6], [700, 0]
+    for bounded in (0, 1):
+        plan = pav.pa_plan(base_shape(lengths_are_bounds=bounded, partition_tokens=512), ctx, q,
+                           win, device=-1)
+        first = min(it[2] for it in plan.items() if it[0] == 0)
+        assert first == (0 if bounded else 5000 - 6 - 700 + 1)
+        st = pav.library().pa_decode_verify_dev(plan.handle, 4, 4, 4, 4, 4, None, None, None, 4,
+                                                None)
+        assert st == pav.PA_E_INVALID
+        plan.close()
 
 
 def test_all_padded_slots_plan_nothing():
