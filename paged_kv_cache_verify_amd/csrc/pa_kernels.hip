@@ -981,7 +981,28 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   // Page ids of every chunk (a page past the item's end repeats the
   // chunk's first page, whose slots the masks then exclude).
   const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
-  for (int i = tid; i < 2 * nch; i += kThreads<D>) {
+  // The loader starts its group's first R - 1 chunks at once, with page ids
+  // read straight from the block table (all of them first, then the loads),
+  // while the other waves fill the page table and load the query.
+  if (loader) {
+    int pa[RG::R - 1], pb[RG::R - 1];
+#pragma unroll
+    for (int k = 0; k < RG::R - 1; ++k) {
+      const int ck = gp + kGroups * k;
+      const int tok0 = tokbase + ck * kChunk;
+      const int pg = tok0 >> 4;
+      pa[k] = ck < nch ? __builtin_amdgcn_readfirstlane(bt[pg]) : 0;
+      pb[k] = ck < nch ? __builtin_amdgcn_readfirstlane(bt[tok0 + kBlock < tv1 ? pg + 1 : pg])
+                       : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < RG::R - 1; ++k)
+      if (gp + kGroups * k < nch)
+        issue_chunk<D, FP8>(A, sm.ring[gp] + k * RG::STAGE, pa[k], pb[k], g, lane);
+  }
+  constexpr int kFillThreads = kGroups * kTileWaves<D> * 64;
+  const int fill_tid = (gp * kTileWaves<D> + (loader ? 0 : r)) * 64 + lane;
+  for (int i = fill_tid; !loader && i < 2 * nch; i += kFillThreads) {
     const int k = i >> 1, which = i & 1;
     const int tok0 = tokbase + k * kChunk;
     const int pg = (tok0 >> 4) + which;
@@ -1026,24 +1047,18 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   // Finish the query and table loads here, with a wait the compiler sees:
   // otherwise it waits for the query inside the chunk loop, where vmcnt(0)
   // would also drain the ring's loads on every chunk.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
-  __syncthreads();  // page ids visible to every wave
+  // (The loader's only loads are its ring's first chunks: it does not wait.)
+  if (!loader) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
+  ring_barrier();  // page ids (and the FP8 query operands) visible to every wave
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
 
-  // Chunk of this wave's group at step k: gp + 2 k. The loader fills the
-  // first R - 1 stages; then per step: the loader waits for its loads of
-  // the step's chunk, the barrier (every group's chunk has landed and every
-  // wave is done with the stage about to be refilled), the loader refills
-  // that stage while the compute waves work. Compute waves never issue or
-  // wait for ring loads, so they never stall behind the load queue.
-  if (loader) {
-    for (int k = 0; k < RG::R - 1 && gp + kGroups * k < nch; ++k) {
-      int pa, pb;
-      chunk_pages(pages_addr, gp + kGroups * k, pa, pb);
-      issue_chunk<D, FP8>(A, ring + k * RG::STAGE, pa, pb, g, lane);
-    }
-  }
+  // Chunk of this wave's group at step k: gp + 2 k. The loader filled the
+  // first R - 1 stages above; then per step: the loader waits for its loads
+  // of the step's chunk, the barrier (every group's chunk has landed and
+  // every wave is done with the stage about to be refilled), the loader
+  // refills that stage while the compute waves work. Compute waves never
+  // issue or wait for ring loads, so they never stall behind the load queue.
   // One step: the loader's wait, the barrier, the loader's refill.
   auto step_begin = [&](int k) __attribute__((always_inline)) {
     if (loader) {  // this step's chunk has landed; the next R - 2 may be pending
@@ -1136,11 +1151,19 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) store_out<D, FP8>(A, ob + 16 * mt, S.o[mt] * rs);
   } else {
+    // Partials go out with nontemporal stores: the reduce kernel reads them
+    // once, and lines kept out of the L2 make the kernel's final write-back
+    // shorter (the partition kernel measured 1.5 us faster on the MTP-5
+    // workload).
     const int64_t pr = (int64_t)it.slot * A.rows_stride + row;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
-      *reinterpret_cast<f32x4*>(A.part_o + pr * D + 16 * mt + 4 * c) = S.o[mt];
-    if (c == 0) *reinterpret_cast<float2*>(A.part_ml + pr * 2) = make_float2(S.m, S.l);
+      __builtin_nontemporal_store(S.o[mt],
+                                  reinterpret_cast<f32x4*>(A.part_o + pr * D + 16 * mt + 4 * c));
+    if (c == 0) {
+      __builtin_nontemporal_store(S.m, A.part_ml + pr * 2);
+      __builtin_nontemporal_store(S.l, A.part_ml + pr * 2 + 1);
+    }
   }
 }
 
