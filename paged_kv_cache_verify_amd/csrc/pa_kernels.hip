@@ -720,8 +720,9 @@ struct Fp8Chunk {
 // Phase 1 of an FP8 chunk, straight from the ring stage st (K codes in the
 // FP8 MFMA's operand order, the V code tile, then the K and V scales):
 // S^T = K Q^T on the codes, once with each query term, times the per-token
-// K scale and the row's query scale; masks; the V code columns (transposing
-// byte reads, issued while the QK products run). Returns whether a row's
+// K scale (the row's query scale is folded into scale_log2, which the
+// caller passes per row); masks; the V code columns (transposing byte
+// reads, issued while the QK products run). Returns whether a row's
 // reference must move before the chunk's probabilities are taken.
 template <int D>
 __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chunk<D>& X,
@@ -792,8 +793,10 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
           (__attribute__((address_space(3))) i32x2*)(uintptr_t)(vbase ^ (uint32_t)(mt << 4)));
   }
 
+  // (The row's query scale rides in scale_log2: the caller passes
+  // sigma log2(e) times it.)
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) X.sc[bb] = X.sc[bb] * (ksc[bb] * S.Q.qs);
+  for (int bb = 0; bb < 2; ++bb) X.sc[bb] = X.sc[bb] * ksc[bb];
   X.interior = chunk_interior(tok0, tv0, tv1, L, q, W);
   if (!X.interior) {
     asm volatile("");  // a real branch
@@ -1088,6 +1091,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
     // inside the loop the compiler moves the accumulators between
     // registers on every chunk.)
     Fp8Chunk<D> X;
+    const float sl = A.scale_log2 * S.Q.qs;  // per row: the query scale folded in
     int k = 0;
     for (;;) {
       bool moved = false;
@@ -1096,16 +1100,16 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
         step_begin(k);
         if (active && ck < nch) {
           if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
-                              tv1, L, q, W, A.scale_log2, lane, sm.qbuf + r * 8192)) {
+                              tv1, L, q, W, sl, lane, sm.qbuf + r * 8192)) {
             moved = true;
             break;
           }
-          chunk_finish<D>(S, X, tv0, tv1, A.scale_log2, lane);
+          chunk_finish<D>(S, X, tv0, tv1, sl, lane);
         }
       }
       if (!moved) break;
       rescale(S, X.mx);
-      chunk_finish<D>(S, X, tv0, tv1, A.scale_log2, lane);
+      chunk_finish<D>(S, X, tv0, tv1, sl, lane);
       ++k;
     }
   }
@@ -1176,7 +1180,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
 // partition lanes then combine through LDS in a fixed order. Two shapes:
 // few partials per pair (all columns of a row in one workgroup of 128
 // threads) and many (a quarter of the columns, 32 partition lanes).
-template <int D, int COLS, int PARTS>
+template <int D, int COLS, int PARTS, int U>
 __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
   constexpr int DSPLIT = D / 4 / COLS;
   __shared__ float s_m[PARTS][COLS];
@@ -1198,8 +1202,8 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
   const int64_t ostride = (int64_t)A.rows_stride * D;
 
   // Batches of U partials: all loads of a batch are in flight together,
-  // then they are folded in order.
-  constexpr int U = 4;
+  // then they are folded in order (PARTS x U covers the few-partials shape
+  // in one batch).
   float M = -INFINITY, z = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = pl; k0 < n; k0 += PARTS * U) {
@@ -1276,18 +1280,22 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
   const unsigned items = (unsigned)n_red * rows_stride;
   if (max_parts <= 32) {  // 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
     if (head_dim == 256)    // half a row per workgroup
-      hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4>), dim3(items * 2), dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4, 8>), dim3(items * 2), dim3(128), 0, stream,
+                         a);
     else if (head_dim == 128)
-      hipLaunchKernelGGL((pa_reduce_kernel<128, 32, 4>), dim3(items), dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<128, 32, 4, 8>), dim3(items), dim3(128), 0, stream, a);
     else
-      hipLaunchKernelGGL((pa_reduce_kernel<64, 16, 8>), dim3(items), dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<64, 16, 8, 4>), dim3(items), dim3(128), 0, stream, a);
   } else {  // 8 column lanes x 32 partition lanes per eighth, quarter or half of a row
     if (head_dim == 256)
-      hipLaunchKernelGGL((pa_reduce_kernel<256, 8, 32>), dim3(items * 8), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<256, 8, 32, 4>), dim3(items * 8), dim3(256), 0, stream,
+                         a);
     else if (head_dim == 128)
-      hipLaunchKernelGGL((pa_reduce_kernel<128, 8, 32>), dim3(items * 4), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<128, 8, 32, 4>), dim3(items * 4), dim3(256), 0, stream,
+                         a);
     else
-      hipLaunchKernelGGL((pa_reduce_kernel<64, 8, 32>), dim3(items * 2), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_kernel<64, 8, 32, 4>), dim3(items * 2), dim3(256), 0, stream,
+                         a);
   }
   return hipGetLastError();
 }
