@@ -57,11 +57,6 @@ struct Cfg {
   static_assert(BLKB >= 1024, "a 1 KiB slab must stay inside one page");
 };
 
-// Compute waves per token group (one per 16-row tile): four, so up to 64
-// packed rows; three at D 256, whose waves need more registers (up to 48
-// rows).
-template <int D>
-constexpr int kTileWaves = D == 256 ? 3 : 4;
 
 // bf16 QK: lane group c holds d = 32 s + 8 c .. +8 of contraction step s
 // (64 contiguous bytes per token across the 4 lane groups); Q uses the same
@@ -189,14 +184,17 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // The LDS rings: one per token group.
 // ---------------------------------------------------------------------------
 
-constexpr int kGroups = 2;  // token groups per workgroup
-template <int D>
-constexpr int kGroupWaves = kTileWaves<D> + 1;  // a group's compute waves and its loader
-template <int D>
-constexpr int kThreads = 64 * kGroups * kGroupWaves<D>;
+// A workgroup's layout: NG token groups of TW row-tile waves and one
+// loader each. Two groups of four tile waves serve up to 64 rows (three at
+// D 256, up to 48 rows); FP8 at D 128 with at most 48 rows uses four groups
+// of three, so that every SIMD hosts three compute waves and one loader.
+template <int NG, int TW>
+constexpr int kThreads = 64 * NG * (TW + 1);
 // LDS per group: the workgroup holds most of a CU's 160 KiB.
-constexpr int kGroupRingBytes = 76 * 1024;
+template <int NG>
+constexpr int kGroupRingBytes = NG == 2 ? 76 * 1024 : 38 * 1024;
 
+// One ring stage: a 32-token chunk.
 template <int D, bool FP8>
 struct Ring {
   using C = Cfg<D, FP8>;
@@ -204,18 +202,24 @@ struct Ring {
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  static constexpr int R0 = kGroupRingBytes / STAGE;
-  static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
   // Loads per chunk, all issued by the group's loader wave: 1 KiB ones of
   // K and V, and (FP8) one of the scales.
   static constexpr int T = 2 * C::KLD + C::VLD + (FP8 ? 1 : 0);
+  static_assert(STAGE % 256 == 0 && KB % 256 == 0, "stage addresses keep their low 8 bits zero");
+};
+
+// A group's ring of R stages.
+template <int D, bool FP8, int NG>
+struct RingN : Ring<D, FP8> {
+  using S = Ring<D, FP8>;
+  static constexpr int R0 = kGroupRingBytes<NG> / S::STAGE;
+  static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
   static_assert(R >= 3, "the ring needs enough stages to keep loads in flight");
   // Loads the loader may still have in flight when its group starts on a
   // step: the step's chunk must have landed, the next R - 2 may be pending.
-  static constexpr int WAIT = (R - 2) * T;
+  static constexpr int WAIT = (R - 2) * S::T;
   static_assert(WAIT <= 63, "vmcnt holds at most 63");
-  static constexpr int RING = R * STAGE;         // bytes per group
-  static_assert(STAGE % 256 == 0 && KB % 256 == 0, "stage addresses keep their low 8 bits zero");
+  static constexpr int RING = R * S::STAGE;      // bytes per group
 };
 
 // FP8 at D 256 keeps the query operands of each row tile in LDS (both
@@ -224,15 +228,15 @@ struct Ring {
 // two terms of the two contraction steps, 2 KiB each, in lane order.
 template <int D, bool FP8>
 constexpr bool kQInLds = FP8 && D == 256;
-template <int D, bool FP8>
-constexpr int kQBytes = kQInLds<D, FP8> ? kTileWaves<D> * 4 * 2048 : 16;
+template <int D, bool FP8, int TW>
+constexpr int kQBytes = kQInLds<D, FP8> ? TW * 4 * 2048 : 16;
 
 // The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
 // FP8 V reads rely on the low 8 bits of a stage's address being zero.
-template <int D, bool FP8>
+template <int D, bool FP8, int NG, int TW>
 struct Smem {
-  alignas(1024) unsigned char ring[kGroups][Ring<D, FP8>::RING];
-  alignas(16) unsigned char qbuf[kQBytes<D, FP8>];
+  alignas(1024) unsigned char ring[NG][RingN<D, FP8, NG>::RING];
+  alignas(16) unsigned char qbuf[kQBytes<D, FP8, TW>];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
@@ -947,17 +951,22 @@ __device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t*
   }
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs A) {
+template <int D, bool FP8, int NG, int TW>
+__global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
-  using RG = Ring<D, FP8>;
-  __shared__ Smem<D, FP8> sm;
+  using RG = RingN<D, FP8, NG>;
+  constexpr int GW = TW + 1;  // waves per group
+  __shared__ Smem<D, FP8, NG, TW> sm;
   const WorkItem it = A.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int gp = w / kGroupWaves<D>, r = w % kGroupWaves<D>;  // token group, row tile
-  const bool loader = r == kTileWaves<D>;                      // the group's loader
+  // Token group gp, role r (row tile r < TW, or the loader). With four
+  // groups of four waves the roles rotate by group: wave w runs on SIMD
+  // w mod 4, so every SIMD then hosts three tile waves and one loader.
+  const int gp = w / GW, slot = w % GW;
+  const int r = (NG == 4 && GW == 4) ? (slot + gp) % GW : slot;
+  const bool loader = r == TW;
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
@@ -979,7 +988,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   const int tokbase = (tv0 >> 4) << 4;
   // <= kMaxItemChunks: [tv0, tv1) lies inside the planned item
   const int nch = tv1 > tv0 ? (tv1 - tokbase + kChunk - 1) / kChunk : 0;
-  const int nst = (nch + kGroups - 1) / kGroups;           // steps: one chunk per group
+  const int nst = (nch + NG - 1) / NG;  // steps: one chunk per group
 
   // Page ids of every chunk (a page past the item's end repeats the
   // chunk's first page, whose slots the masks then exclude).
@@ -991,7 +1000,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
     int pa[RG::R - 1], pb[RG::R - 1];
 #pragma unroll
     for (int k = 0; k < RG::R - 1; ++k) {
-      const int ck = gp + kGroups * k;
+      const int ck = gp + NG * k;
       const int tok0 = tokbase + ck * kChunk;
       const int pg = tok0 >> 4;
       pa[k] = ck < nch ? __builtin_amdgcn_readfirstlane(bt[pg]) : 0;
@@ -1000,11 +1009,11 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
     }
 #pragma unroll
     for (int k = 0; k < RG::R - 1; ++k)
-      if (gp + kGroups * k < nch)
+      if (gp + NG * k < nch)
         issue_chunk<D, FP8>(A, sm.ring[gp] + k * RG::STAGE, pa[k], pb[k], g, lane);
   }
-  constexpr int kFillThreads = kGroups * kTileWaves<D> * 64;
-  const int fill_tid = (gp * kTileWaves<D> + (loader ? 0 : r)) * 64 + lane;
+  constexpr int kFillThreads = NG * TW * 64;
+  const int fill_tid = (gp * TW + (loader ? 0 : r)) * 64 + lane;
   for (int i = fill_tid; !loader && i < 2 * nch; i += kFillThreads) {
     const int k = i >> 1, which = i & 1;
     const int tok0 = tokbase + k * kChunk;
@@ -1065,11 +1074,11 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   // One step: the loader's wait, the barrier, the loader's refill.
   auto step_begin = [&](int k) __attribute__((always_inline)) {
     if (loader) {  // this step's chunk has landed; the next R - 2 may be pending
-      if (gp + kGroups * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
+      if (gp + NG * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
       else wait_vm<0>();
     }
     ring_barrier();
-    const int cn = gp + kGroups * (k + RG::R - 1);
+    const int cn = gp + NG * (k + RG::R - 1);
     if (loader && cn < nch) {
       int pa, pb;
       chunk_pages(pages_addr, cn, pa, pb);
@@ -1078,7 +1087,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
   };
   if constexpr (!FP8) {
     for (int k = 0; k < nst; ++k) {
-      const int ck = gp + kGroups * k;
+      const int ck = gp + NG * k;
       step_begin(k);
       if (active && ck < nch)
         compute_chunk<D>(S, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0, tv1, L,
@@ -1096,7 +1105,7 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
     for (;;) {
       bool moved = false;
       for (; k < nst; ++k) {
-        const int ck = gp + kGroups * k;
+        const int ck = gp + NG * k;
         step_begin(k);
         if (active && ck < nch) {
           if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
@@ -1114,28 +1123,36 @@ __global__ __launch_bounds__(kThreads<D>, 1) void pa_partition_kernel(KernelArgs
     }
   }
 
-  // ---- Merge the groups: group 1's waves hand (m, l, O) of their tile to
-  // group 0's through LDS (the rings are free once every wave is past the
-  // barrier; every wave's loads have completed, its last wait was vmcnt(0)).
+  // ---- Merge the groups: the waves of groups 1..NG-1 hand (m, l, O) of
+  // their tile to group 0's through LDS, which merges them in group order
+  // (the rings are free once every wave is past the barrier; every wave's
+  // loads have completed, its last wait was vmcnt(0)).
   S.l = xlane_sum4(S.l);
   __syncthreads();
-  f32x4* xo = reinterpret_cast<f32x4*>(&sm.ring[0][0]);       // [tile][mt][lane]
-  float* xm = reinterpret_cast<float*>(&sm.ring[0][0]) + kTileWaves<D> * C::MT * 64 * 4;  // [tile][lane][m, l]
-  if (gp == 1 && active) {
+  constexpr int kXo = TW * C::MT * 64;                              // f32x4 per group
+  f32x4* xo = reinterpret_cast<f32x4*>(&sm.ring[0][0]);           // [group-1][tile][mt][lane]
+  float* xm = reinterpret_cast<float*>(xo + (NG - 1) * kXo);       // [group-1][tile][lane][m, l]
+  static_assert((NG - 1) * (kXo * 16 + TW * 64 * 8) <= NG * RG::RING, "merge fits the rings");
+  if (gp > 0 && active) {
+    f32x4* o = xo + (gp - 1) * kXo;
+    float* ml = xm + ((gp - 1) * TW + r) * 128;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) xo[(r * C::MT + mt) * 64 + lane] = S.o[mt];
-    xm[(r * 64 + lane) * 2] = S.m;
-    xm[(r * 64 + lane) * 2 + 1] = S.l;
+    for (int mt = 0; mt < C::MT; ++mt) o[(r * C::MT + mt) * 64 + lane] = S.o[mt];
+    ml[lane * 2] = S.m;
+    ml[lane * 2 + 1] = S.l;
   }
   __syncthreads();
-  if (gp == 1 || !active) return;
-  {
-    const float m1 = xm[(r * 64 + lane) * 2], l1 = xm[(r * 64 + lane) * 2 + 1];
+  if (gp > 0 || !active) return;
+#pragma unroll
+  for (int j = 0; j < NG - 1; ++j) {
+    const f32x4* o = xo + j * kXo;
+    const float* ml = xm + (j * TW + r) * 128;
+    const float m1 = ml[lane * 2], l1 = ml[lane * 2 + 1];
     const float M = fmaxf(S.m, m1);
     const float a0 = (S.m == -INFINITY) ? 0.f : fast_exp2(S.m - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = S.o[mt] * a0 + xo[(r * C::MT + mt) * 64 + lane] * a1;
+    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = S.o[mt] * a0 + o[(r * C::MT + mt) * 64 + lane] * a1;
     S.l = S.l * a0 + l1 * a1;
     S.m = M;
   }
@@ -1257,19 +1274,26 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
                             hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   const dim3 grid(n_items);
+  if (ntmax < 1) return hipErrorInvalidValue;
   if (head_dim == 256) {  // FP8 KV only, at most 48 rows
-    if (!fp8 || ntmax < 1 || ntmax > kTileWaves<256>) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pa_partition_kernel<256, true>), grid, dim3(kThreads<256>), 0, stream, a);
+    if (!fp8 || ntmax > 3) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_partition_kernel<256, true, 2, 3>), grid, dim3(kThreads<2, 3>), 0,
+                       stream, a);
     return hipGetLastError();
   }
-  if (ntmax < 1 || ntmax > kTileWaves<128>) return hipErrorInvalidValue;
-  const dim3 block(kThreads<128>);
+  if (ntmax > 4) return hipErrorInvalidValue;
+  const dim3 block(kThreads<2, 4>);
   if (head_dim == 128) {
-    if (fp8) hipLaunchKernelGGL((pa_partition_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((pa_partition_kernel<128, false>), grid, block, 0, stream, a);
+    if (fp8 && ntmax <= 3)
+      hipLaunchKernelGGL((pa_partition_kernel<128, true, 4, 3>), grid, dim3(kThreads<4, 3>), 0,
+                         stream, a);
+    else if (fp8)
+      hipLaunchKernelGGL((pa_partition_kernel<128, true, 2, 4>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_partition_kernel<128, false, 2, 4>), grid, block, 0, stream, a);
   } else {
-    if (fp8) hipLaunchKernelGGL((pa_partition_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((pa_partition_kernel<64, false>), grid, block, 0, stream, a);
+    if (fp8) hipLaunchKernelGGL((pa_partition_kernel<64, true, 2, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((pa_partition_kernel<64, false, 2, 4>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
