@@ -961,11 +961,15 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // Token group gp, role r (row tile r < TW, or the loader). With four
-  // groups of four waves the roles rotate by group: wave w runs on SIMD
-  // w mod 4, so every SIMD then hosts three tile waves and one loader.
+  // Token group gp, role r (row tile r < TW, or the loader). The roles
+  // rotate by group so that the tile waves spread over the SIMDs (wave w
+  // runs on SIMD w mod 4): with four groups of three tile waves every SIMD
+  // hosts three of them and one loader; with two groups the second group's
+  // tiles 0 and 1 sit on the two SIMDs the first group's tiles 0 and 1 do
+  // not use, so items of up to two tiles run one compute wave per SIMD.
+  constexpr int kRot = NG == 4 ? 1 : (GW == 5 ? 4 : 2);
   const int gp = w / GW, slot = w % GW;
-  const int r = (NG == 4 && GW == 4) ? (slot + gp) % GW : slot;
+  const int r = (slot + gp * kRot) % GW;
   const bool loader = r == TW;
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
