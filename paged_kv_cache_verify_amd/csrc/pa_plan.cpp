@@ -36,6 +36,7 @@ struct SeqInfo {
   int32_t n_parts;   // work items per KV head
   int32_t piece;     // keys per work item (the last one may be shorter)
   int32_t slot_base; // partial slot of (kv head 0, part 0) when n_parts > 1
+  double cost;       // relative time per key of this sequence's items
 };
 
 }  // namespace
@@ -183,40 +184,65 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
 
 // Work items of (at most) `piece` keys for every active sequence, counted
 // over all KV heads.
-int64_t count_items(const std::vector<SeqInfo>& seqs, int Hkv, int64_t piece) {
+// Relative time per key of an item with `rows` packed rows. bf16 KV is
+// bound by its bytes (1). FP8 KV is bound by per-CU compute: the busiest
+// SIMD's compute waves per chunk, c, depend on the item's row tiles and the
+// workgroup layout (four groups of three tile waves: c = tiles / 4; two
+// rotated groups: 1/2 for up to two tiles, else 1), and the measured
+// compute time of one wave-chunk is about 2.7 chunks' streaming time.
+double item_cost(const pa_shape& s, int rows, int ntmax) {
+  if (s.kv_dtype != PA_FP8_E4M3) return 1.0;
+  const int tiles = (rows + 15) / 16;
+  const double c = (s.head_dim == 128 && ntmax <= 3) ? 0.25 * tiles : (tiles <= 2 ? 0.5 : 1.0);
+  return 1.0 + (4.0 / 3.0) * c;
+}
+
+// Keys per item of a sequence for a cost-weighted item size P: a multiple
+// of 32, within [lo_keys, kMaxItemKeys].
+int64_t keys_for(double P, double cost, int64_t lo_keys) {
+  const int64_t k = ((int64_t)(P / cost) / kChunk) * kChunk;
+  return std::min<int64_t>(kMaxItemKeys, std::max<int64_t>(lo_keys, k));
+}
+
+int64_t count_items(const std::vector<SeqInfo>& seqs, int Hkv, double P, int64_t lo_keys) {
   int64_t n = 0;
   for (const SeqInfo& si : seqs) {
     if (si.q_len == 0) continue;
     const int64_t span = si.ctx_len - (si.lo / kBlock) * kBlock;
+    const int64_t piece = keys_for(P, si.cost, lo_keys);
     n += Hkv * ((span + piece - 1) / piece);
   }
   return n;
 }
 
-// Item size when the caller leaves the choice to the plan. One workgroup
-// runs per CU, so the plan looks for the smallest size (a multiple of 32
-// keys) whose items fit one round on the device; the workgroups then start
-// together and each streams about the same number of keys. When no size up
-// to the item limit fits one round, items of about a third of a round's
-// share keep the rounds' tails short.
-int64_t auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus) {
-  int64_t total = 0;
+// Item size, in cost-weighted keys, when the caller leaves the choice to the
+// plan. One workgroup runs per CU, so the plan looks for the smallest size
+// whose items fit one round on the device; the workgroups then start
+// together and each runs for about the same time (a sequence whose items
+// cost less per key gets more keys per item). When no size up to the item
+// limit fits one round, items of about a third of a round's share keep the
+// rounds' tails short.
+double auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus, int64_t& lo_keys) {
+  double total = 0.0, max_cost = 1.0;
   for (const SeqInfo& si : seqs)
-    if (si.q_len > 0) total += (int64_t)Hkv * (si.ctx_len - (si.lo / kBlock) * kBlock);
-  if (total == 0) return kChunk;
-  auto round32 = [](int64_t x) { return ((x + kChunk - 1) / kChunk) * kChunk; };
-  if (count_items(seqs, Hkv, kMaxItemKeys) <= cus) {
-    int64_t lo = std::max<int64_t>(kChunk, round32((total + cus - 1) / cus)), hi = kMaxItemKeys;
-    lo = std::min(lo, hi);
-    while (lo < hi) {  // smallest multiple of 32 in [lo, hi] that fits one round
-      const int64_t mid = round32((lo + hi) / 2);
-      if (mid >= hi) break;
-      if (count_items(seqs, Hkv, mid) <= cus) hi = mid;
-      else lo = mid + kChunk;
+    if (si.q_len > 0) {
+      total += (double)Hkv * (si.ctx_len - (si.lo / kBlock) * kBlock) * si.cost;
+      max_cost = std::max(max_cost, si.cost);
+    }
+  lo_keys = kChunk;
+  if (total == 0.0) return kChunk;
+  const double p_max = (double)kMaxItemKeys * max_cost;
+  if (count_items(seqs, Hkv, p_max, lo_keys) <= cus) {
+    double lo = total / cus / 2, hi = p_max;
+    for (int it = 0; it < 40; ++it) {  // the smallest size that fits one round
+      const double mid = 0.5 * (lo + hi);
+      if (count_items(seqs, Hkv, mid, lo_keys) <= cus) hi = mid;
+      else lo = mid;
     }
     return hi;
   }
-  return std::min<int64_t>(kMaxItemKeys, std::max<int64_t>(512, round32(total / (3LL * cus))));
+  lo_keys = 512;
+  return total / (3.0 * cus);
 }
 
 }  // namespace
@@ -291,8 +317,10 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     // partition_tokens is that size for every sequence; otherwise each
     // sequence is cut into as few equal pieces of at most the plan's item
     // size as will do.
-    const int64_t limit = s.partition_tokens > 0 ? s.partition_tokens
-                                                 : auto_piece(p->seqs, Hkv, cus);
+    const int ntmax = (rows_stride + 15) / 16;
+    for (SeqInfo& si : p->seqs) si.cost = item_cost(s, si.q_len * G, ntmax);
+    int64_t lo_keys = kChunk;
+    const double weighted = s.partition_tokens > 0 ? 0.0 : auto_piece(p->seqs, Hkv, cus, lo_keys);
     int64_t slots = 0;
     int32_t largest = 0;
     for (int b = 0; b < B; ++b) {
@@ -300,6 +328,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       if (si.q_len == 0) continue;
       const int a = (si.lo / kBlock) * kBlock;
       const int span = si.ctx_len - a;
+      const int64_t limit = s.partition_tokens > 0 ? s.partition_tokens
+                                                   : keys_for(weighted, si.cost, lo_keys);
       si.n_parts = (int32_t)((span + limit - 1) / limit);
       if (s.partition_tokens > 0) {
         si.piece = (int32_t)limit;
