@@ -185,11 +185,13 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
 // Work items of (at most) `piece` keys for every active sequence, counted
 // over all KV heads.
 // Relative time per key of an item with `rows` packed rows. bf16 KV is
-// bound by its bytes (1). FP8 KV is bound by per-CU compute: the busiest
-// SIMD's compute waves per chunk, c, depend on the item's row tiles and the
-// workgroup layout (four groups of three tile waves: c = tiles / 4; two
-// rotated groups: 1/2 for up to two tiles, else 1), and the measured
-// compute time of one wave-chunk is about 2.7 chunks' streaming time.
+// bound by its bytes (1). With FP8 KV a chunk costs a fixed part (its
+// streaming, the softmax's bookkeeping, the ring's barriers) plus a part
+// that grows with the busiest SIMD's compute waves per chunk, c, which
+// depends on the item's row tiles and the workgroup layout (four groups of
+// three tile waves: c = tiles / 4; two rotated groups: 1/2 for up to two
+// tiles, else 1). The slope 4/3 fits measured partition times of items with
+// two and three row tiles (about 0.5 and 0.6 us per chunk).
 double item_cost(const pa_shape& s, int rows, int ntmax) {
   if (s.kv_dtype != PA_FP8_E4M3) return 1.0;
   const int tiles = (rows + 15) / 16;
