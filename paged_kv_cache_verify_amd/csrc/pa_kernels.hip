@@ -43,6 +43,7 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, bool FP8>
 struct Cfg {
@@ -538,28 +539,6 @@ __device__ __forceinline__ f32x4 pv_tile(bf16x8 v, bf16x8 p_hi, bf16x8 p_lo, f32
   return mfma_bf16(v, p_lo, o);
 }
 
-// e4m3 (bias 7, largest finite 448) nearest to y, |y| <= 448, ties to the
-// even code, as an fp32 value: below 2^-6 the e4m3 values are the multiples
-// of 2^-9 (scaling by 2^9 is exact, rint rounds to even); above, fp32's 23
-// mantissa bits are rounded to 3 (a carry moves into the exponent).
-// (Both candidates are computed and one is selected: straight-line code.)
-__device__ __forceinline__ float e4m3_round(float y) {
-  const float a = fabsf(y);
-  const float sub = __builtin_rintf(a * 512.0f) * (1.0f / 512.0f);
-  const uint32_t b = __float_as_uint(a);
-  const float nrm = __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u);
-  return __builtin_copysignf(a < 0.015625f ? sub : nrm, y);
-}
-
-// The e4m3 code of an fp32 value that is exactly an e4m3 value.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  const uint32_t sub = (uint32_t)(a * 512.0f);
-  const uint32_t nrm = (__float_as_uint(a) >> 20) - (120u << 3);
-  return sign | (a < 0.015625f ? sub : nrm);
-}
-
 // One chunk for the wave's 16-row tile, bf16 KV: kv is the ring stage (K of
 // the two pages in operand order, then the V tile).
 template <int D>
@@ -922,6 +901,9 @@ __device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t*
   e = e < -100 ? -100 : e;
   const float inv = __uint_as_float((uint32_t)(127 + 7 - e) << 23);  // 2^(7 - e)
   Q.qs = __uint_as_float((uint32_t)(127 - 7 + e) << 23);             // 2^(e - 7)
+  // hi and lo come from the hardware conversion (v_cvt_pk_fp8_f32, nearest
+  // even; |y| < 2^8 stays far from e4m3's overflow), the residual y - hi
+  // from converting hi back: both exact in fp32.
 #pragma unroll
   for (int ks = 0; ks < C::KS8; ++ks) {
     uint32_t hw[8], lw[8];
@@ -929,19 +911,20 @@ __device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t*
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {  // dwords 2v, 2v + 1: four values each
-        uint32_t hb = 0, lb = 0;
+        float y[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const uint32_t w = raw[ks][v][2 * h + (b >> 1)];
-          const float x = __uint_as_float((b & 1) ? (w & 0xFFFF0000u) : (w << 16));
-          const float y = x * inv;
-          const float yh = e4m3_round(y);
-          const float yl = e4m3_round(y - yh);
-          hb |= e4m3_code(yh) << (8 * b);
-          lb |= e4m3_code(yl) << (8 * b);
+          y[b] = __uint_as_float((b & 1) ? (w & 0xFFFF0000u) : (w << 16)) * inv;
         }
-        hw[2 * v + h] = hb;
-        lw[2 * v + h] = lb;
+        int hb = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        hb = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], hb, true);
+        const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hb, false);
+        const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hb, true);
+        int lb = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] - h01[0], y[1] - h01[1], 0, false);
+        lb = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] - h23[0], y[3] - h23[1], lb, true);
+        hw[2 * v + h] = (uint32_t)hb;
+        lw[2 * v + h] = (uint32_t)lb;
       }
     }
     Q.hi[ks] = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3],
