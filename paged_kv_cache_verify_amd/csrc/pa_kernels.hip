@@ -980,19 +980,31 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   // Page ids of every chunk (a page past the item's end repeats the
   // chunk's first page, whose slots the masks then exclude).
   const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
-  // The loader starts its group's first R - 1 chunks at once, with page ids
-  // read straight from the block table (all of them first, then the loads),
-  // while the other waves fill the page table and load the query.
+  // The loader starts its group's first R - 1 chunks at once while the
+  // other waves fill the page table and load the query. One vector load
+  // brings every page id those chunks need: lane j < 2 (R - 1) reads chunk
+  // j / 2's page j % 2 (the chunk's first page where its second lies past
+  // the item). (Scalar loads of the same entries came back up to 2.5 us
+  // later than vector loads, and held the later groups' loaders back.)
   if (loader) {
+    int pid = 0;
+    {
+      const int k = lane >> 1, which = lane & 1;
+      const int ck = gp + NG * k;
+      if (lane < 2 * (RG::R - 1) && ck < nch) {
+        const int tok0 = tokbase + ck * kChunk;
+        const int pg = (tok0 >> 4) + which;
+        pid = bt[(which == 0 || tok0 + kBlock < tv1) ? pg : pg - 1];
+      }
+    }
+    // The wait is the loader's only one here (no chunk is in flight yet);
+    // with it explicit, the compiler adds none between the chunks' loads.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
     int pa[RG::R - 1], pb[RG::R - 1];
 #pragma unroll
     for (int k = 0; k < RG::R - 1; ++k) {
-      const int ck = gp + NG * k;
-      const int tok0 = tokbase + ck * kChunk;
-      const int pg = tok0 >> 4;
-      pa[k] = ck < nch ? __builtin_amdgcn_readfirstlane(bt[pg]) : 0;
-      pb[k] = ck < nch ? __builtin_amdgcn_readfirstlane(bt[tok0 + kBlock < tv1 ? pg + 1 : pg])
-                       : 0;
+      pa[k] = __builtin_amdgcn_readlane(pid, 2 * k);
+      pb[k] = __builtin_amdgcn_readlane(pid, 2 * k + 1);
     }
 #pragma unroll
     for (int k = 0; k < RG::R - 1; ++k)
@@ -1011,14 +1023,19 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   // The wave's row tile: row = 16 r + lane % 16 (padding rows mirror the
   // last real row and carry a zero query).
   WaveState<D, FP8> S;
-  {
+  S.m = -INFINITY;
+  S.l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The loader skips the query (a wave-uniform branch): on a path shared
+  // with the query loads it would also execute their vmcnt(0) and wait for
+  // its ring's first chunks before the barrier below.
+  if (!loader) {
     const int row = 16 * r + n;
     const bool live = active && row < rows;
     const int rr = live ? row : rows - 1;
     const int i = rr / G, hh = rr % G;
     S.prow = L - q + i;
-    S.m = -INFINITY;
-    S.l = 0.f;
     const uint16_t* qp = A.q + ((int64_t)(it.q_off + i) * Hq + g * G + hh) * D;
     if constexpr (!FP8) {
 #pragma unroll
@@ -1040,14 +1057,10 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
         }
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Finish the query and table loads here, with a wait the compiler sees:
+    // otherwise it waits for the query inside the chunk loop.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
   }
-  // Finish the query and table loads here, with a wait the compiler sees:
-  // otherwise it waits for the query inside the chunk loop, where vmcnt(0)
-  // would also drain the ring's loads on every chunk.
-  // (The loader's only loads are its ring's first chunks: it does not wait.)
-  if (!loader) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
   ring_barrier();  // page ids (and the FP8 query operands) visible to every wave
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
