@@ -244,3 +244,24 @@ def test_all_padded_slots_plan_nothing():
     plan = pav.pa_plan(base_shape(num_seqs=3), [10, 20, 30], [0, 0, 0], None, device=-1)
     assert plan.info()["work_items"] == 0 and plan.info()["kv_bytes"] == 0
     plan.close()
+
+
+def test_fp8_plan_weights_items_by_row_tiles():
+    """With FP8 KV and the plan's own item size, a sequence whose rows make
+    fewer row tiles (less compute per key) gets longer items; bf16 KV, bound
+    by bytes, sizes every sequence alike. Items still fit one round of the
+    device's CUs and tile every sequence's keys."""
+    ctx = [16000] * 8
+    q = [2, 6] * 4  # 8 q heads per KV head: 16 rows (one tile) or 48 rows (three)
+    for kv in ("fp8", "bf16"):
+        shape = base_shape(num_seqs=8, kv_dtype=kv, num_blocks=8192, max_blocks_per_seq=1024)
+        plan = pav.pa_plan(shape, ctx, q, None, device=-1)
+        items = check_worklist(plan, ctx, q, None, 2)
+        assert len(items) <= 256
+        longest = {qq: max(k1 - k0 for (b, _, k0, k1, _) in items if q[b] == qq) for qq in (2, 6)}
+        if kv == "fp8":
+            # weights 1 + (4/3)(tiles/4): 4/3 for one tile, 2 for three
+            assert 1.3 < longest[2] / longest[6] < 1.7
+        else:
+            assert longest[2] == longest[6]
+        plan.close()
