@@ -223,21 +223,11 @@ struct RingN : Ring<D, FP8> {
   static constexpr int RING = R * S::STAGE;      // bytes per group
 };
 
-// FP8 at D 256 keeps the query operands of each row tile in LDS (both
-// token groups read the same tile), which frees 32 registers per compute
-// wave: the accumulators then stay in place across the loop. Per tile: the
-// two terms of the two contraction steps, 2 KiB each, in lane order.
-template <int D, bool FP8>
-constexpr bool kQInLds = FP8 && D == 256;
-template <int D, bool FP8, int TW>
-constexpr int kQBytes = kQInLds<D, FP8> ? TW * 4 * 2048 : 16;
-
 // The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
 // FP8 V reads rely on the low 8 bits of a stage's address being zero.
 template <int D, bool FP8, int NG, int TW>
 struct Smem {
   alignas(1024) unsigned char ring[NG][RingN<D, FP8, NG>::RING];
-  alignas(16) unsigned char qbuf[kQBytes<D, FP8, TW>];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
@@ -544,8 +534,7 @@ __device__ __forceinline__ f32x4 pv_tile(bf16x8 v, bf16x8 p_hi, bf16x8 p_lo, f32
 template <int D>
 __device__ __forceinline__ void compute_chunk(WaveState<D, false>& S, const unsigned char* kv,
                                               int tok0, int tv0, int tv1, int L, int q, int W,
-                                              float scale_log2, int lane,
-                                              const unsigned char* = nullptr) {
+                                              float scale_log2, int lane) {
   using C = Cfg<D, false>;
   using RG = Ring<D, false>;
   const int c = lane >> 4;
@@ -710,8 +699,7 @@ struct Fp8Chunk {
 template <int D>
 __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chunk<D>& X,
                                              const unsigned char* st, int tok0, int tv0, int tv1,
-                                             int L, int q, int W, float scale_log2, int lane,
-                                             const unsigned char* qb) {
+                                             int L, int q, int W, float scale_log2, int lane) {
   using C = Cfg<D, true>;
   using RG = Ring<D, true>;
   const int c = lane >> 4;
@@ -739,15 +727,8 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
       }
       const i32x8 kop = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      if constexpr (kQInLds<D, true>) {
-        const i32x8 qh = *reinterpret_cast<const i32x8*>(qb + (2 * ks) * 2048 + lane * 32);
-        const i32x8 ql = *reinterpret_cast<const i32x8*>(qb + (2 * ks + 1) * 2048 + lane * 32);
-        acc = mfma_fp8(kop, qh, acc);
-        acc = mfma_fp8(kop, ql, acc);
-      } else {
-        acc = mfma_fp8(kop, S.Q.hi[ks], acc);
-        acc = mfma_fp8(kop, S.Q.lo[ks], acc);
-      }
+      acc = mfma_fp8(kop, S.Q.hi[ks], acc);
+      acc = mfma_fp8(kop, S.Q.lo[ks], acc);
     }
     X.sc[bb] = acc;
   }
@@ -1046,22 +1027,12 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
       }
     } else {
       load_query_fp8<D>(S.Q, qp, live, c);
-      if constexpr (kQInLds<D, FP8>) {
-        if (gp == 0 && active) {  // both groups' wave r read tile r's operands
-          unsigned char* qb = sm.qbuf + r * 8192 + lane * 32;
-#pragma unroll
-          for (int ks = 0; ks < C::KS8; ++ks) {
-            *reinterpret_cast<i32x8*>(qb + (2 * ks) * 2048) = S.Q.hi[ks];
-            *reinterpret_cast<i32x8*>(qb + (2 * ks + 1) * 2048) = S.Q.lo[ks];
-          }
-        }
-      }
     }
     // Finish the query and table loads here, with a wait the compiler sees:
     // otherwise it waits for the query inside the chunk loop.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
   }
-  ring_barrier();  // page ids (and the FP8 query operands) visible to every wave
+  ring_barrier();  // the page table is visible to every wave
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
 
@@ -1109,7 +1080,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
         step_begin(k);
         if (active && ck < nch) {
           if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
-                              tv1, L, q, W, sl, lane, sm.qbuf + r * 8192)) {
+                              tv1, L, q, W, sl, lane)) {
             moved = true;
             break;
           }
