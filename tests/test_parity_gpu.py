@@ -201,6 +201,14 @@ EDGES = {
     "FP8 with windows and sinks": dict(kv_dtype="fp8", ctx_lens=[2500, 300], q_lens=[6, 8],
                                        window=[1000, 0], sinks_rows=[True, True]),
     "bf16 output": dict(out_dtype="bf16", ctx_lens=[1200, 17], q_lens=[6, 6]),
+    # at most 48 rows: the FP8 head-128 layout of four token groups, where
+    # short items leave some groups without a chunk
+    "FP8 four token groups, short and page-boundary lengths": dict(
+        kv_dtype="fp8", ctx_lens=[1, 15, 16, 17, 31, 32, 33, 100, 129],
+        q_lens=[1, 2, 6, 3, 6, 4, 5, 6, 1]),
+    "FP8 four token groups, windows and sinks": dict(
+        kv_dtype="fp8", ctx_lens=[2000, 300, 64, 5000], q_lens=[6, 2, 4, 3],
+        window=[100, 0, 7, 0], sinks_rows=[True, True, False, False]),
     "head dim 256, FP8, ragged": dict(head_dim=256, kv_dtype="fp8", num_q_heads=8,
                                       num_kv_heads=1, ctx_lens=[700, 129, 33, 16, 6],
                                       q_lens=[6, 1, 5, 3, 6]),
