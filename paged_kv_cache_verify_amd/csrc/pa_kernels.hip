@@ -214,7 +214,10 @@ template <int D, bool FP8, int NG>
 struct RingN : Ring<D, FP8> {
   using S = Ring<D, FP8>;
   static constexpr int R0 = kGroupRingBytes<NG> / S::STAGE;
-  static constexpr int R = R0 < 8 ? R0 : 8;      // stages per group
+  // Stages per group, at most four: the loader issues R - 1 chunks in the
+  // prologue, and with eight stages (FP8 at D 128, more than 48 rows) that
+  // early burst measured ~10 us slower over a multi-round call than four.
+  static constexpr int R = R0 < 4 ? R0 : 4;
   static_assert(R >= 3, "the ring needs enough stages to keep loads in flight");
   // Loads the loader may still have in flight when its group starts on a
   // step: the step's chunk must have landed, the next R - 2 may be pending.
