@@ -116,12 +116,20 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
   asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// max(a, b) in one instruction (see max3 below: the operands are never NaN
+// where these are used, so the quieting fmaxf adds is not needed).
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float xlane_max4(float v) {
   float a = v, b = v;
   swap16(a, b);
-  float c = fmaxf(a, b), d = c;
+  float c = max2(a, b), d = c;
   swap32(c, d);
-  return fmaxf(c, d);
+  return max2(c, d);
 }
 
 __device__ __forceinline__ float xlane_sum4(float v) {
@@ -145,7 +153,7 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 
 __device__ __forceinline__ float max8(const f32x4 (&x)[2]) {
   return max3(max3(x[0][0], x[0][1], x[0][2]), max3(x[0][3], x[1][0], x[1][1]),
-              __builtin_fmaxf(x[1][2], x[1][3]));
+              max2(x[1][2], x[1][3]));
 }
 
 // LDS V tile of one wave: [32 tokens][D] elements (bf16, or FP8 codes),
@@ -487,17 +495,16 @@ __device__ __forceinline__ void chunk_probs(WaveState<D, FP8>& S, const f32x4 (&
                                             const f32x4 (&vs)[2], float scale_log2,
                                             float (&pw)[8]) {
   const float msafe = (S.m == -INFINITY) ? 0.f : S.m;
-  float ps = 0.f;
+  float p[8];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = fast_exp2(__builtin_fmaf(sc[bb][i], scale_log2, -msafe));
-      ps += p;
-      pw[4 * bb + i] = FP8 ? p * vs[bb][i] : p;
+      p[4 * bb + i] = fast_exp2(__builtin_fmaf(sc[bb][i], scale_log2, -msafe));
+      pw[4 * bb + i] = FP8 ? p[4 * bb + i] * vs[bb][i] : p[4 * bb + i];
     }
   }
-  S.l += ps;
+  S.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
 template <int D, bool FP8>
@@ -699,10 +706,21 @@ struct Fp8Chunk {
 // caller passes per row); masks; the V code columns (transposing byte
 // reads, issued while the QK products run). Returns whether a row's
 // reference must move before the chunk's probabilities are taken.
+// The lane's byte offset in the V code tile for the transposing reads of
+// output tile 0: lanes 2r, 2r + 1 of a group address token 16 (r / 4) +
+// 4 c + r % 4 (the P^T order), bytes 8 k of the tile's 16-byte chunk.
+template <int D>
+__device__ __forceinline__ uint32_t vcode_lane_off(int lane) {
+  const int rr = (lane & 15) >> 1, k = lane & 1;
+  const int t = 16 * (rr >> 2) + 4 * (lane >> 4) + (rr & 3);
+  return t * Cfg<D, true>::ROWB + (vswz<D, true>(t) << 4) + 8 * k;
+}
+
 template <int D>
 __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chunk<D>& X,
                                              const unsigned char* st, int tok0, int tv0, int tv1,
-                                             int L, int q, int W, float scale_log2, int lane) {
+                                             int L, int q, int W, float scale_log2, int lane,
+                                             uint32_t voff) {
   using C = Cfg<D, true>;
   using RG = Ring<D, true>;
   const int c = lane >> 4;
@@ -742,18 +760,15 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
     X.vs[bb] = *reinterpret_cast<const f32x4*>(scl + 128 + (bb * 16 + 4 * c) * 4);
   }
 
-  // ---- V code columns: lanes 2r, 2r + 1 of a group address token
-  // 16 (r / 4) + 4 c + r % 4 (the P^T order), bytes 16 mt + 8 k. The stage
-  // and the token row are 256-byte and ROWB aligned and the swizzle only
-  // touches the 16-byte chunk bits, so tile mt's address is a fixed XOR of
-  // one base. (The compute waves issue no direct-to-LDS loads, so the
+  // ---- V code columns (voff: vcode_lane_off), bytes 16 mt + 8 k of the
+  // lane's token. The stage and the token row are 256-byte and ROWB aligned
+  // and the swizzle only touches the 16-byte chunk bits, so tile mt's
+  // address is a fixed XOR of one base. (The compute waves issue no direct-to-LDS loads, so the
   // compiler's own waits around these reads cost nothing.)
   {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // keep the per-tile addresses out of the loop
-    const int rr = (ln & 15) >> 1, k = ln & 1;
-    const int t = 16 * (rr >> 2) + 4 * (ln >> 4) + (rr & 3);
-    const uint32_t vbase = lds_addr(st + RG::KB) + t * C::ROWB + (vswz<D, true>(t) << 4) + 8 * k;
+    uint32_t vo = voff;
+    asm volatile("" : "+v"(vo));  // keep the per-tile addresses out of the loop
+    const uint32_t vbase = lds_addr(st + RG::KB) + vo;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
       X.vcode[mt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -782,9 +797,7 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
   // softmax reference by log2(w) - 1 (rare: |V| above 896).
   float extra = 0.f;
   {
-    const float vmax = max3(max3(X.vs[0][0], X.vs[0][1], X.vs[0][2]),
-                            max3(X.vs[0][3], X.vs[1][0], X.vs[1][1]),
-                            __builtin_fmaxf(X.vs[1][2], X.vs[1][3]));
+    const float vmax = max8(X.vs);
     if (__any(vmax > 2.0f)) {
       asm volatile("");  // a real branch
       extra = __builtin_amdgcn_logf(xlane_max4(vmax)) - 1.0f;
@@ -1075,6 +1088,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
     // registers on every chunk.)
     Fp8Chunk<D> X;
     const float sl = A.scale_log2 * S.Q.qs;  // per row: the query scale folded in
+    const uint32_t voff = vcode_lane_off<D>(lane);
     int k = 0;
     for (;;) {
       bool moved = false;
@@ -1083,7 +1097,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
         step_begin(k);
         if (active && ck < nch) {
           if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
-                              tv1, L, q, W, sl, lane)) {
+                              tv1, L, q, W, sl, lane, voff)) {
             moved = true;
             break;
           }
