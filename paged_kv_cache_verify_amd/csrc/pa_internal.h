@@ -114,9 +114,11 @@ struct VerdictArgs {
 hipError_t launch_verdict(const VerdictArgs& a, hipStream_t stream);
 
 // ntmax: row tiles of 16 the kernel is built for (ceil(max q x G / 16));
-// items with fewer rows skip the missing tiles. One workgroup per CU.
+// items with fewer rows skip the missing tiles. occ: workgroups meant to
+// share a CU, 1 (items fit one round) or 2 (more items than CUs, bf16 KV
+// only).
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
-                            hipStream_t stream);
+                            int occ, hipStream_t stream);
 // rows_stride: the most rows any reduce item has; max_parts: the most
 // partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,

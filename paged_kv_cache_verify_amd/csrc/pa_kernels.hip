@@ -197,11 +197,20 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // loader each. Two groups of four tile waves serve up to 64 rows (three at
 // D 256, up to 48 rows); FP8 at D 128 with at most 48 rows uses four groups
 // of three, so that every SIMD hosts three compute waves and one loader.
+//
+// OCC is the number of workgroups meant to share a CU. One (OCC 1) holds
+// most of the CU's 160 KiB of LDS; that suits a plan whose items fit one
+// round. When there are more items than CUs, two smaller workgroups (OCC 2,
+// at most 80 KiB each) share a CU, so that one streams while the other is
+// in its prologue or epilogue. (FP8 KV keeps one: its items are bound by
+// compute per SIMD, and the role rotation below only spreads the compute
+// waves over the SIMDs within one workgroup; two one-group workgroups
+// measured 6% slower on a mixed FP8 batch.)
 template <int NG, int TW>
 constexpr int kThreads = 64 * NG * (TW + 1);
-// LDS per group: the workgroup holds most of a CU's 160 KiB.
-template <int NG>
-constexpr int kGroupRingBytes = NG == 2 ? 76 * 1024 : 38 * 1024;
+// Ring bytes per group.
+template <int NG, int OCC>
+constexpr int kGroupRingBytes = OCC == 2 ? 72 * 1024 / NG : (NG == 2 ? 76 * 1024 : 38 * 1024);
 
 // One ring stage: a 32-token chunk.
 template <int D, bool FP8>
@@ -218,10 +227,10 @@ struct Ring {
 };
 
 // A group's ring of R stages.
-template <int D, bool FP8, int NG>
+template <int D, bool FP8, int NG, int OCC>
 struct RingN : Ring<D, FP8> {
   using S = Ring<D, FP8>;
-  static constexpr int R0 = kGroupRingBytes<NG> / S::STAGE;
+  static constexpr int R0 = kGroupRingBytes<NG, OCC> / S::STAGE;
   // Stages per group, at most four: the loader issues R - 1 chunks in the
   // prologue, and with eight stages (FP8 at D 128, more than 48 rows) that
   // early burst measured ~10 us slower over a multi-round call than four.
@@ -236,9 +245,9 @@ struct RingN : Ring<D, FP8> {
 
 // The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
 // FP8 V reads rely on the low 8 bits of a stage's address being zero.
-template <int D, bool FP8, int NG, int TW>
+template <int D, bool FP8, int NG, int TW, int OCC>
 struct Smem {
-  alignas(1024) unsigned char ring[NG][RingN<D, FP8, NG>::RING];
+  alignas(1024) unsigned char ring[NG][RingN<D, FP8, NG, OCC>::RING];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
 };
 
@@ -931,12 +940,14 @@ __device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t*
   }
 }
 
-template <int D, bool FP8, int NG, int TW>
+template <int D, bool FP8, int NG, int TW, int OCC>
 __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
-  using RG = RingN<D, FP8, NG>;
+  using RG = RingN<D, FP8, NG, OCC>;
   constexpr int GW = TW + 1;  // waves per group
-  __shared__ Smem<D, FP8, NG, TW> sm;
+  using SM = Smem<D, FP8, NG, TW, OCC>;
+  static_assert(OCC == 1 || sizeof(SM) <= 80 * 1024, "two workgroups share a CU's LDS");
+  __shared__ SM sm;
   const WorkItem it = A.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1258,30 +1269,33 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
   store_out<D, false>(A, ((int64_t)(ri.q_off + i) * Hq + h) * D + d, tot * (1.0f / Z));
 }
 
+// One template instance per (head dim, KV dtype, layout, occupancy).
+template <int D, bool FP8, int NG, int TW, int OCC>
+static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
+                     dim3(kThreads<NG, TW>), 0, stream, a);
+}
+
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
-                            hipStream_t stream) {
+                            int occ, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  const dim3 grid(n_items);
-  if (ntmax < 1) return hipErrorInvalidValue;
-  if (head_dim == 256) {  // FP8 KV only, at most 48 rows
+  if (ntmax < 1 || (occ != 1 && occ != 2)) return hipErrorInvalidValue;
+  if (head_dim == 256) {  // FP8 KV only, at most 48 rows; one workgroup per CU
     if (!fp8 || ntmax > 3) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pa_partition_kernel<256, true, 2, 3>), grid, dim3(kThreads<2, 3>), 0,
-                       stream, a);
+    launch_one<256, true, 2, 3, 1>(a, n_items, stream);
     return hipGetLastError();
   }
   if (ntmax > 4) return hipErrorInvalidValue;
-  const dim3 block(kThreads<2, 4>);
+  if (fp8 && occ != 1) return hipErrorInvalidValue;  // FP8 runs one workgroup per CU
   if (head_dim == 128) {
-    if (fp8 && ntmax <= 3)
-      hipLaunchKernelGGL((pa_partition_kernel<128, true, 4, 3>), grid, dim3(kThreads<4, 3>), 0,
-                         stream, a);
-    else if (fp8)
-      hipLaunchKernelGGL((pa_partition_kernel<128, true, 2, 4>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((pa_partition_kernel<128, false, 2, 4>), grid, block, 0, stream, a);
+    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1>(a, n_items, stream);
+    else if (fp8) launch_one<128, true, 2, 4, 1>(a, n_items, stream);
+    else if (occ == 1) launch_one<128, false, 2, 4, 1>(a, n_items, stream);
+    else launch_one<128, false, 1, 4, 2>(a, n_items, stream);
   } else {
-    if (fp8) hipLaunchKernelGGL((pa_partition_kernel<64, true, 2, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((pa_partition_kernel<64, false, 2, 4>), grid, block, 0, stream, a);
+    if (fp8) launch_one<64, true, 2, 4, 1>(a, n_items, stream);
+    else if (occ == 1) launch_one<64, false, 2, 4, 1>(a, n_items, stream);
+    else launch_one<64, false, 1, 4, 2>(a, n_items, stream);
   }
   return hipGetLastError();
 }

@@ -54,6 +54,7 @@ struct pa_plan_s {
   int64_t n_slots = 0;
   std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
   int32_t max_parts = 0;        // most partials of any split pair
+  int32_t occ = 1;              // partition workgroups per CU (2 when items exceed one round)
   std::vector<int32_t> tokens;  // [T][2]: sequence, position of each new token
   std::vector<int32_t> seq_rows;  // [B][2]: first verify row, verify rows (q)
   WorkItem* d_items = nullptr;
@@ -373,6 +374,11 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       }
     }
     p->partition_tokens = s.partition_tokens > 0 ? s.partition_tokens : largest;
+    // More items than one round of one workgroup per CU: with bf16 KV two
+    // smaller workgroups share each CU, so one streams while the other
+    // starts or finishes an item (FP8 items are bound by compute and keep
+    // one workgroup per CU).
+    p->occ = ((int64_t)p->items.size() > cus && s.kv_dtype == PA_BF16) ? 2 : 1;
     for (const WorkItem& it : p->items) {
       // A workgroup keeps the page ids of at most kMaxItemChunks chunks.
       const int span = it.key_end - (it.key_begin / kBlock) * kBlock;
@@ -494,7 +500,7 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   if (plan->ev_before && (e = hipEventRecord(plan->ev_before, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, (plan->rows_stride + 15) / 16,
-                       st);
+                       plan->occ, st);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
