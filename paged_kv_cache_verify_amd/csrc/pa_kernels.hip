@@ -1269,6 +1269,65 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
   store_out<D, false>(A, ((int64_t)(ri.q_off + i) * Hq + h) * D + d, tot * (1.0f / Z));
 }
 
+// The same merge for pairs with few partials (at most 32): one thread per
+// (row, four columns) folds every partial of its row in index order, with
+// the loads of up to U partials in flight at once; a workgroup covers RB
+// consecutive rows of one pair across all D columns, so each wave reads
+// whole rows of a partial (contiguous 512-byte runs at D 128) and no thread
+// waits on another. Grid: (reduce item, block of RB rows). For many split
+// pairs this launches a fraction of the workgroups of one per row (16,384
+// on a mixed batch of 256 split pairs with a 64-row stride, where the merge
+// was mostly latency).
+template <int D, int RB, int U>
+__global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A) {
+  constexpr int COLS = D / 4;
+  const int nblk = (A.rows_stride + RB - 1) / RB;
+  const ReduceItem ri = A.red[blockIdx.x / nblk];
+  const int row = (blockIdx.x % nblk) * RB + (int)threadIdx.x / COLS;
+  const int G = A.group, Hq = A.num_q_heads;
+  if (row >= ri.q_len * G) return;  // no barrier follows
+  const int d = ((int)threadIdx.x % COLS) * 4;
+  const int n = ri.n_parts;
+  const float* ml = A.part_ml + ((int64_t)ri.slot_base * A.rows_stride + row) * 2;
+  const float* po = A.part_o + ((int64_t)ri.slot_base * A.rows_stride + row) * D + d;
+  const int64_t mstride = (int64_t)A.rows_stride * 2;
+  const int64_t ostride = (int64_t)A.rows_stride * D;
+
+  float M = -INFINITY, z = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += U) {
+    float2 v[U];
+    f32x4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u;
+      v[u] = make_float2(-INFINITY, 0.f);
+      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k < n) {
+        v[u] = *reinterpret_cast<const float2*>(ml + k * mstride);
+        o[u] = *reinterpret_cast<const f32x4*>(po + k * ostride);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // m = -inf: no key of that item is visible to the row.
+      const float Mn = fmaxf(M, v[u].x);
+      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+      const float wk = (v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - Mn);
+      acc = acc * a + o[u] * wk;
+      z = z * a + v[u].y * wk;
+      M = Mn;
+    }
+  }
+  const int i = row / G, hh = row % G;
+  const int h = ri.kv_head * G + hh;
+  const float zs = sink_log2(A, ri.seq, h);
+  const float Mx = fmaxf(M, zs);
+  const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
+  const float Z = z * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
+  store_out<D, false>(A, ((int64_t)(ri.q_off + i) * Hq + h) * D + d, acc * (a / Z));
+}
+
 // One template instance per (head dim, KV dtype, layout, occupancy).
 template <int D, bool FP8, int NG, int TW, int OCC>
 static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream) {
@@ -1304,8 +1363,20 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
                          int max_parts, hipStream_t stream) {
   if (n_red <= 0) return hipSuccess;
   const unsigned items = (unsigned)n_red * rows_stride;
-  if (max_parts <= 32) {  // 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
-    if (head_dim == 256)    // half a row per workgroup
+  if (max_parts <= 32 && items >= 2048) {
+    // Many split pairs: 256 threads = RB rows x D / 4 column lanes, 16
+    // partials in flight per thread. (With few pairs, e.g. 16 pairs of 48
+    // rows, this makes too few workgroups to pull the partials quickly,
+    // and the one-row shape below with its partition lanes is faster.)
+    const unsigned blocks = (unsigned)n_red * ((rows_stride + 1024 / head_dim - 1) / (1024 / head_dim));
+    if (head_dim == 256)
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16>), dim3(blocks), dim3(256), 0, stream, a);
+    else if (head_dim == 128)
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16>), dim3(blocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16>), dim3(blocks), dim3(256), 0, stream, a);
+  } else if (max_parts <= 32) {  // one row: 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
+    if (head_dim == 256)  // half a row per workgroup
       hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4, 8>), dim3(items * 2), dim3(128), 0, stream,
                          a);
     else if (head_dim == 128)

@@ -227,6 +227,46 @@ def test_edge(name, P):
     check(edge(name, **EDGES[name]), f"edge: {name}", partition_tokens=P)
 
 
+# Many split pairs with at most 32 partials each: the reduce then runs its
+# row-block shape (a workgroup per block of rows of a pair, every partial
+# folded by one thread per row and four columns), at every head dim.
+def _many_pairs(B, seed, qs):
+    g = np.random.default_rng(seed)
+    ctx = g.integers(40, 900, size=B).tolist()
+    q = [qs[b % len(qs)] for b in range(B)]
+    return ctx, q
+
+
+MANY_PAIRS = {
+    "head dim 64, bf16, windows and sinks": dict(
+        head_dim=64, num_q_heads=16, num_kv_heads=2, B=24, qs=[1, 2, 3, 4, 5, 6, 7, 8],
+        windowed=True),
+    "head dim 128, bf16": dict(head_dim=128, num_q_heads=16, num_kv_heads=2, B=32,
+                               qs=[6, 3, 8, 1]),
+    "head dim 128, FP8, windows and sinks": dict(
+        head_dim=128, kv_dtype="fp8", num_q_heads=16, num_kv_heads=2, B=32, qs=[4, 6, 2, 5],
+        windowed=True),
+    "head dim 256, FP8": dict(head_dim=256, kv_dtype="fp8", num_q_heads=8, num_kv_heads=1,
+                              B=48, qs=[6, 1, 5, 3]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY_PAIRS))
+def test_many_split_pairs(name):
+    kw = dict(MANY_PAIRS[name])
+    B, qs, windowed = kw.pop("B"), kw.pop("qs"), kw.pop("windowed", False)
+    ctx, q = _many_pairs(B, 11 + B, qs)
+    if windowed:
+        kw["window"] = [(0 if b % 3 else 150) for b in range(B)]
+        kw["sinks_rows"] = [b % 2 == 0 for b in range(B)]
+    wl = edge(f"many split pairs, {name}", ctx_lens=ctx, q_lens=q, **kw)
+    rows = max(q) * (kw["num_q_heads"] // kw["num_kv_heads"])
+    assert B * kw["num_kv_heads"] * rows >= 2048  # the row-block reduce shape
+    # 32-key items: every pair with more than 32 visible keys is split, into
+    # at most 29 partials (contexts below 900 keys)
+    check(wl, f"many split pairs: {name}", partition_tokens=32)
+
+
 def test_split_invariance():
     """The partitioning is a re-association of one sum: any split agrees."""
     wl = workloads.make(2, scale_ctx=1 / 8, num_seqs=3, out_dtype="fp32")
