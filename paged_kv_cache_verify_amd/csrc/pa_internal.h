@@ -47,7 +47,10 @@ struct ReduceItem {
   int32_t n_parts;
   int32_t q_len;
   int32_t q_off;
-  int32_t pad[2];
+  // first level of a two-level merge: the first-level slot this chunk of
+  // the pair's partials merges into (unused otherwise)
+  int32_t out_slot;
+  int32_t pad;
 };
 
 struct KernelArgs {
@@ -74,6 +77,10 @@ struct KernelArgs {
   // Device context lengths [B] read at run time (the plan's lengths are
   // then upper bounds), or null: the plan's own lengths.
   const int32_t* dev_ctx;
+  // First-level scratch of the two-level merge (pairs with more than 32
+  // partials): [chunks][rows_stride][D] and [chunks][rows_stride][2].
+  float* l1_o;
+  float* l1_ml;
 };
 
 // The new tokens of a verify step, for the paged KV append kernel.
@@ -123,6 +130,10 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
 // partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
                          int max_parts, hipStream_t stream);
+// First level of the two-level merge: a.red lists n_chunks chunks of a
+// pair's partials (ReduceItem::out_slot: the first-level slot written).
+hipError_t launch_reduce_stage1(const KernelArgs& a, int n_chunks, int head_dim, int rows_stride,
+                                hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int head_dim, bool fp8, hipStream_t stream);
 
 }  // namespace pav

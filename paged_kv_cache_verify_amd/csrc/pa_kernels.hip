@@ -1278,7 +1278,13 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
 // pairs this launches a fraction of the workgroups of one per row (16,384
 // on a mixed batch of 256 split pairs with a 64-row stride, where the merge
 // was mostly latency).
-template <int D, int RB, int U>
+//
+// STAGE1: the first level of a two-level merge for pairs with more than 32
+// partials. The item is then one chunk of a pair's partials (slot_base,
+// n_parts), and the thread writes the chunk's merged partial (O relative
+// to its maximum, the maximum, the sum: the partition kernel's format) to
+// slot out_slot of the first-level scratch instead of the output.
+template <int D, int RB, int U, bool STAGE1>
 __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A) {
   constexpr int COLS = D / 4;
   const int nblk = (A.rows_stride + RB - 1) / RB;
@@ -1318,6 +1324,12 @@ __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A
       z = z * a + v[u].y * wk;
       M = Mn;
     }
+  }
+  if constexpr (STAGE1) {
+    const int64_t pr = (int64_t)ri.out_slot * A.rows_stride + row;
+    *reinterpret_cast<f32x4*>(A.l1_o + pr * D + d) = acc;
+    if (d == 0) *reinterpret_cast<float2*>(A.l1_ml + pr * 2) = make_float2(M, z);
+    return;
   }
   const int i = row / G, hh = row % G;
   const int h = ri.kv_head * G + hh;
@@ -1359,6 +1371,23 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
   return hipGetLastError();
 }
 
+hipError_t launch_reduce_stage1(const KernelArgs& a, int n_chunks, int head_dim, int rows_stride,
+                                hipStream_t stream) {
+  if (n_chunks <= 0) return hipSuccess;
+  const unsigned blocks =
+      (unsigned)n_chunks * ((rows_stride + 1024 / head_dim - 1) / (1024 / head_dim));
+  if (head_dim == 256)
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, true>), dim3(blocks), dim3(256), 0, stream,
+                       a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, true>), dim3(blocks), dim3(256), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, true>), dim3(blocks), dim3(256), 0, stream,
+                       a);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,
                          int max_parts, hipStream_t stream) {
   if (n_red <= 0) return hipSuccess;
@@ -1370,11 +1399,11 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
     // and the one-row shape below with its partition lanes is faster.)
     const unsigned blocks = (unsigned)n_red * ((rows_stride + 1024 / head_dim - 1) / (1024 / head_dim));
     if (head_dim == 256)
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
     else if (head_dim == 128)
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
   } else if (max_parts <= 32) {  // one row: 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
     if (head_dim == 256)  // half a row per workgroup
       hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4, 8>), dim3(items * 2), dim3(128), 0, stream,

@@ -65,6 +65,14 @@ struct pa_plan_s {
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
   float* d_part_ml = nullptr;
+  // Two-level merge (some pair has more than 32 partials): the first level
+  // folds chunks of at most ceil(n / 32) partials into first-level slots,
+  // and `red` then lists each pair's first-level slots.
+  std::vector<ReduceItem> red1;
+  int64_t l1_slots = 0;
+  ReduceItem* d_red1 = nullptr;
+  float* d_l1_o = nullptr;
+  float* d_l1_ml = nullptr;
   hipEvent_t ev_before = nullptr;
   hipEvent_t ev_after = nullptr;
 };
@@ -97,6 +105,9 @@ void release_device(pa_plan_s* p) {
   if (p->d_red) (void)hipFree(p->d_red);
   if (p->d_part_o) (void)hipFree(p->d_part_o);
   if (p->d_part_ml) (void)hipFree(p->d_part_ml);
+  if (p->d_red1) (void)hipFree(p->d_red1);
+  if (p->d_l1_o) (void)hipFree(p->d_l1_o);
+  if (p->d_l1_ml) (void)hipFree(p->d_l1_ml);
   if (p->d_tokens) (void)hipFree(p->d_tokens);
   if (p->d_seq_rows) (void)hipFree(p->d_seq_rows);
   if (p->d_verdict_val) (void)hipFree(p->d_verdict_val);
@@ -109,6 +120,9 @@ void release_device(pa_plan_s* p) {
   p->d_red = nullptr;
   p->d_part_o = nullptr;
   p->d_part_ml = nullptr;
+  p->d_red1 = nullptr;
+  p->d_l1_o = nullptr;
+  p->d_l1_ml = nullptr;
   if (have && cur != p->device) (void)hipSetDevice(cur);
 }
 
@@ -397,7 +411,37 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
     });
     p->n_slots = slots;
-    p->scratch_bytes = slots * rows_stride * ((int64_t)s.head_dim + 2) * 4;
+    // With more than 512 partials in some pair, the pairs are merged in two
+    // levels: chunks of C = ceil(n / 32) consecutive partials fold into at
+    // most 32 first-level partials, which the usual merge then combines.
+    // One level with thousands of partials per row is bound by its 128-byte
+    // reads 24 KiB apart, where chunks read whole rows of consecutive
+    // partials: at 2,048 partials per pair (512-key items over 1 Mi keys)
+    // the call measured 3.2 us faster, while at 128 (8,192-key items) the
+    // second launch made it 3.9 us slower.
+    if (p->max_parts > 512) {
+      int32_t max2 = 0;
+      for (ReduceItem& r : p->red) {
+        const int32_t n = r.n_parts, C = (n + 31) / 32, nch = (n + C - 1) / C;
+        for (int32_t c = 0; c < nch; ++c) {
+          ReduceItem r1 = r;
+          r1.slot_base = r.slot_base + c * C;
+          r1.n_parts = std::min(C, n - c * C);
+          r1.out_slot = (int32_t)(p->l1_slots + c);
+          p->red1.push_back(r1);
+        }
+        r.slot_base = (int32_t)p->l1_slots;
+        r.n_parts = nch;
+        p->l1_slots += nch;
+        max2 = std::max(max2, nch);
+      }
+      p->max_parts = max2;
+      if ((int64_t)p->red1.size() * rows_stride >= (int64_t)INT32_MAX) {
+        delete p;
+        return fail(PA_E_UNSUPPORTED, "the first-level merge list exceeds a 1-D grid");
+      }
+    }
+    p->scratch_bytes = (slots + p->l1_slots) * rows_stride * ((int64_t)s.head_dim + 2) * 4;
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(PA_E_NOMEM, "host allocation of the work list failed");
@@ -428,6 +472,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
   if (e == hipSuccess)
     e = upload((void**)&p->d_red, p->red.data(), p->red.size() * sizeof(ReduceItem));
   if (e == hipSuccess)
+    e = upload((void**)&p->d_red1, p->red1.data(), p->red1.size() * sizeof(ReduceItem));
+  if (e == hipSuccess)
     e = upload((void**)&p->d_tokens, p->tokens.data(), p->tokens.size() * sizeof(int32_t));
   if (e == hipSuccess)
     e = upload((void**)&p->d_seq_rows, p->seq_rows.data(), p->seq_rows.size() * sizeof(int32_t));
@@ -441,6 +487,12 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
                   (size_t)p->n_slots * p->rows_stride * s.head_dim * sizeof(float));
     if (e == hipSuccess)
       e = hipMalloc((void**)&p->d_part_ml, (size_t)p->n_slots * p->rows_stride * 2 * sizeof(float));
+  }
+  if (e == hipSuccess && p->l1_slots > 0) {
+    e = hipMalloc((void**)&p->d_l1_o,
+                  (size_t)p->l1_slots * p->rows_stride * s.head_dim * sizeof(float));
+    if (e == hipSuccess)
+      e = hipMalloc((void**)&p->d_l1_ml, (size_t)p->l1_slots * p->rows_stride * 2 * sizeof(float));
   }
   if (cur != device) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
@@ -504,6 +556,18 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
+  if (!plan->red1.empty()) {
+    // Two-level merge: chunks of the partials into first-level partials,
+    // then the pairs' merge over those.
+    a.red = plan->d_red1;
+    a.l1_o = plan->d_l1_o;
+    a.l1_ml = plan->d_l1_ml;
+    e = launch_reduce_stage1(a, (int)plan->red1.size(), s.head_dim, plan->rows_stride, st);
+    if (e != hipSuccess) return hip_fail(e, "first-level reduce kernel launch");
+    a.red = plan->d_red;
+    a.part_o = plan->d_l1_o;
+    a.part_ml = plan->d_l1_ml;
+  }
   e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, plan->max_parts, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   return PA_OK;

@@ -207,8 +207,10 @@ def test_long_context_partitions():
     info = plan.info()
     assert info["work_items"] == 2 * (1 << 20) // 512
     assert info["kv_bytes"] == 2 * (1 << 20) * 512
-    # partials: one (rows x (D + 2)) fp32 record per item
-    assert info["scratch_bytes"] == info["work_items"] * 48 * (128 + 2) * 4
+    # partials: one (rows x (D + 2)) fp32 record per item, plus the
+    # first-level records of the two-level merge (more than 512 partials per
+    # pair: 2,048 fold in chunks of 64 into 32 per pair)
+    assert info["scratch_bytes"] == (info["work_items"] + 2 * 32) * 48 * (128 + 2) * 4
     plan.close()
 
 

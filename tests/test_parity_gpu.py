@@ -160,7 +160,9 @@ def test_head256_full_one_sequence():
     check(workloads.make(6, num_seqs=1), "workload 6 full, batch 1", strict=True)
 
 
-@pytest.mark.parametrize("P", [None, 512])
+# P = 0: the plan's own items (8,192 keys, one round; what the bench times
+# as "partition auto"); 512: the workload's stated partitions.
+@pytest.mark.parametrize("P", [0, 512])
 def test_long_context_full_sampled(P):
     wl = workloads.make(4)
     mask = np.zeros((1, 16), dtype=np.uint8)
@@ -265,6 +267,25 @@ def test_many_split_pairs(name):
     # 32-key items: every pair with more than 32 visible keys is split, into
     # at most 29 partials (contexts below 900 keys)
     check(wl, f"many split pairs: {name}", partition_tokens=32)
+
+
+# More than 512 partials in a pair (16-key items over more than 8,192 keys):
+# the two-level merge, with short pairs in the same plan whose partials pass
+# through first-level chunks of one.
+TWO_LEVEL = {
+    "head dim 64, bf16, sinks": dict(head_dim=64, ctx_lens=[10000, 40, 300], q_lens=[6, 8, 3],
+                                     sinks_rows=[True, False, True]),
+    "head dim 128, FP8, window": dict(kv_dtype="fp8", ctx_lens=[9000, 700], q_lens=[5, 6],
+                                      window=[8500, 0]),
+    "head dim 256, FP8": dict(head_dim=256, kv_dtype="fp8", num_q_heads=8, num_kv_heads=1,
+                              ctx_lens=[12000, 64], q_lens=[6, 2]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TWO_LEVEL))
+def test_two_level_merge(name):
+    check(edge(f"two-level merge, {name}", **TWO_LEVEL[name]), f"two-level merge: {name}",
+          partition_tokens=16)
 
 
 def test_split_invariance():
