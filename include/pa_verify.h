@@ -136,7 +136,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens,
 
 /*
  * Run one verify-attention call with a plan: the partition kernel, then (if
- * any sequence was split) the log-sum-exp reduce kernel, both enqueued on
+ * any sequence was split) the log-sum-exp reduce kernel (two launches when
+ * some (sequence, KV head) has more than 512 partials), all enqueued on
  * `stream` (a hipStream_t; NULL = the null stream) of the plan's device,
  * which must be the current device. Asynchronous: it allocates nothing,
  * never synchronises, and may be captured in a HIP graph. Pointers are device
@@ -247,6 +248,7 @@ const char* pa_last_error(void);
  *                   sequence, Hkv x (visible keys) x (K + V bytes per token,
  *                   plus 8 bytes of FP8 scales)
  *   scratch_bytes   device bytes of the partial results the plan owns
+ *                   (with the two-level merge, its first-level partials too)
  *   work_items      number of partition work items (workgroups launched)
  *   partition_tokens keys per work item actually used
  */
