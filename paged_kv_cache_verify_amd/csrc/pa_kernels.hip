@@ -772,8 +772,9 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
   // ---- V code columns (voff: vcode_lane_off), bytes 16 mt + 8 k of the
   // lane's token. The stage and the token row are 256-byte and ROWB aligned
   // and the swizzle only touches the 16-byte chunk bits, so tile mt's
-  // address is a fixed XOR of one base. (The compute waves issue no direct-to-LDS loads, so the
-  // compiler's own waits around these reads cost nothing.)
+  // address is a fixed XOR of one base. (The compute waves issue no
+  // direct-to-LDS loads, so the compiler's own waits around these reads
+  // cost nothing.)
   {
     uint32_t vo = voff;
     asm volatile("" : "+v"(vo));  // keep the per-tile addresses out of the loop
@@ -1279,11 +1280,12 @@ __global__ __launch_bounds__(COLS * PARTS) void pa_reduce_kernel(KernelArgs A) {
 // on a mixed batch of 256 split pairs with a 64-row stride, where the merge
 // was mostly latency).
 //
-// STAGE1: the first level of a two-level merge for pairs with more than 32
-// partials. The item is then one chunk of a pair's partials (slot_base,
-// n_parts), and the thread writes the chunk's merged partial (O relative
-// to its maximum, the maximum, the sum: the partition kernel's format) to
-// slot out_slot of the first-level scratch instead of the output.
+// STAGE1: the first level of the two-level merge (plans with more than 512
+// partials in some pair). The item is then one chunk of a pair's partials
+// (slot_base, n_parts), and the thread writes the chunk's merged partial
+// (O relative to its maximum, the maximum, the sum: the partition kernel's
+// format) to slot out_slot of the first-level scratch instead of the
+// output.
 template <int D, int RB, int U, bool STAGE1>
 __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A) {
   constexpr int COLS = D / 4;
@@ -1377,14 +1379,14 @@ hipError_t launch_reduce_stage1(const KernelArgs& a, int n_chunks, int head_dim,
   const unsigned blocks =
       (unsigned)n_chunks * ((rows_stride + 1024 / head_dim - 1) / (1024 / head_dim));
   if (head_dim == 256)
-    hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, true>), dim3(blocks), dim3(256), 0, stream,
-                       a);
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, true>),
+                       dim3(blocks), dim3(256), 0, stream, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, true>), dim3(blocks), dim3(256), 0, stream,
-                       a);
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, true>),
+                       dim3(blocks), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, true>), dim3(blocks), dim3(256), 0, stream,
-                       a);
+    hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, true>),
+                       dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1397,14 +1399,19 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
     // partials in flight per thread. (With few pairs, e.g. 16 pairs of 48
     // rows, this makes too few workgroups to pull the partials quickly,
     // and the one-row shape below with its partition lanes is faster.)
-    const unsigned blocks = (unsigned)n_red * ((rows_stride + 1024 / head_dim - 1) / (1024 / head_dim));
+    const unsigned rb = 1024 / head_dim;  // rows per workgroup
+    const unsigned blocks = (unsigned)n_red * ((rows_stride + rb - 1) / rb);
     if (head_dim == 256)
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<256, 4, 16, false>),
+                         dim3(blocks), dim3(256), 0, stream, a);
     else if (head_dim == 128)
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<128, 8, 16, false>),
+                         dim3(blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, false>), dim3(blocks), dim3(256), 0, stream, a);
-  } else if (max_parts <= 32) {  // one row: 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes
+      hipLaunchKernelGGL((pa_reduce_rows_kernel<64, 16, 16, false>),
+                         dim3(blocks), dim3(256), 0, stream, a);
+  } else if (max_parts <= 32) {
+    // One row: 32 (D 128, 256) or 16 column lanes x 4 or 8 partition lanes.
     if (head_dim == 256)  // half a row per workgroup
       hipLaunchKernelGGL((pa_reduce_kernel<256, 32, 4, 8>), dim3(items * 2), dim3(128), 0, stream,
                          a);

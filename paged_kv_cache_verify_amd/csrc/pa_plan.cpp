@@ -65,7 +65,7 @@ struct pa_plan_s {
   ReduceItem* d_red = nullptr;
   float* d_part_o = nullptr;
   float* d_part_ml = nullptr;
-  // Two-level merge (some pair has more than 32 partials): the first level
+  // Two-level merge (some pair has more than 512 partials): the first level
   // folds chunks of at most ceil(n / 32) partials into first-level slots,
   // and `red` then lists each pair's first-level slots.
   std::vector<ReduceItem> red1;
