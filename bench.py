@@ -17,8 +17,9 @@ Timing: the K timed steps are one replay of a HIP graph that captured them
 device synchronisations on both sides, gives ms_per_step.
 
 Roofline: the partition kernel dominates; its duration is read from HIP
-events recorded around it on the call's stream (pa_set_partition_events)
-in an eager pass over the same calls.
+events attached to its launch on the call's stream (pa_set_partition_events:
+the events take the kernel's own start and end timestamps) in an eager pass
+over the same calls.
 """
 
 from __future__ import annotations

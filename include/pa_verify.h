@@ -267,9 +267,11 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
 
 /*
  * Optional timing hook: when both are non-NULL (hipEvent_t handles on the
- * plan's device), every later pa_decode_verify records `before` just ahead of
- * the partition kernel and `after` right behind it, on the call's stream.
- * Pass NULLs to stop. Recording is the only effect; results are unchanged.
+ * plan's device), every later pa_decode_verify launches the partition kernel
+ * with the two events attached (hipExtLaunchKernelGGL), so `before` and
+ * `after` take that kernel's own start and end timestamps on the call's
+ * stream. Pass NULLs to stop (a call to be captured in a graph should run
+ * without them). Timing is the only effect; results are unchanged.
  */
 pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
 

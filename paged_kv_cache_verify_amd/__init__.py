@@ -237,8 +237,8 @@ def pa_free(plan: Plan) -> None:
 
 
 def pa_set_partition_events(plan: Plan, before=None, after=None) -> None:
-    """Record torch.cuda.Event handles around the partition kernel (or stop,
-    with None)."""
+    """Attach torch.cuda.Event handles to the partition kernel's launch, which
+    then takes its start and end timestamps (or stop, with None)."""
     for ev in (before, after):
         if ev is not None and not ev.cuda_event:
             ev.record()  # torch creates its HIP event on the first record

@@ -124,8 +124,10 @@ hipError_t launch_verdict(const VerdictArgs& a, hipStream_t stream);
 // items with fewer rows skip the missing tiles. occ: workgroups meant to
 // share a CU, 1 (items fit one round) or 2 (more items than CUs, bf16 KV
 // only).
+// ev_start, ev_stop: optional timing events taken by the launch itself.
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
-                            int occ, hipStream_t stream);
+                            int occ, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 // rows_stride: the most rows any reduce item has; max_parts: the most
 // partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,

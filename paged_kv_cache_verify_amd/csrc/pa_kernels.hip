@@ -29,6 +29,7 @@
 // x GQA group, per-token FP8 KV scales, a partition kernel and a reducer);
 // ATOM #3091 (Summary: 16-token pages through a block table, stores masked
 // by row liveness).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -1342,33 +1343,42 @@ __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A
   store_out<D, false>(A, ((int64_t)(ri.q_off + i) * Hq + h) * D + d, acc * (a / Z));
 }
 
-// One template instance per (head dim, KV dtype, layout, occupancy).
+// One template instance per (head dim, KV dtype, layout, occupancy). With
+// timing events the launch carries them itself (hipExtLaunchKernelGGL), so
+// they take the kernel's own start and end timestamps, as a kernel trace
+// does, rather than those of marker packets around its dispatch.
 template <int D, bool FP8, int NG, int TW, int OCC>
-static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
-                     dim3(kThreads<NG, TW>), 0, stream, a);
+static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
+  if (ev_start && ev_stop)
+    hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
+                          dim3(kThreads<NG, TW>), 0, stream, ev_start, ev_stop, 0, a);
+  else
+    hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
+                       dim3(kThreads<NG, TW>), 0, stream, a);
 }
 
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
-                            int occ, hipStream_t stream) {
+                            int occ, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop) {
   if (n_items <= 0) return hipSuccess;
   if (ntmax < 1 || (occ != 1 && occ != 2)) return hipErrorInvalidValue;
   if (head_dim == 256) {  // FP8 KV only, at most 48 rows; one workgroup per CU
     if (!fp8 || ntmax > 3) return hipErrorInvalidValue;
-    launch_one<256, true, 2, 3, 1>(a, n_items, stream);
+    launch_one<256, true, 2, 3, 1>(a, n_items, stream, ev_start, ev_stop);
     return hipGetLastError();
   }
   if (ntmax > 4) return hipErrorInvalidValue;
   if (fp8 && occ != 1) return hipErrorInvalidValue;  // FP8 runs one workgroup per CU
   if (head_dim == 128) {
-    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1>(a, n_items, stream);
-    else if (fp8) launch_one<128, true, 2, 4, 1>(a, n_items, stream);
-    else if (occ == 1) launch_one<128, false, 2, 4, 1>(a, n_items, stream);
-    else launch_one<128, false, 1, 4, 2>(a, n_items, stream);
+    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1>(a, n_items, stream, ev_start, ev_stop);
+    else if (fp8) launch_one<128, true, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
+    else if (occ == 1) launch_one<128, false, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
+    else launch_one<128, false, 1, 4, 2>(a, n_items, stream, ev_start, ev_stop);
   } else {
-    if (fp8) launch_one<64, true, 2, 4, 1>(a, n_items, stream);
-    else if (occ == 1) launch_one<64, false, 2, 4, 1>(a, n_items, stream);
-    else launch_one<64, false, 1, 4, 2>(a, n_items, stream);
+    if (fp8) launch_one<64, true, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
+    else if (occ == 1) launch_one<64, false, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
+    else launch_one<64, false, 1, 4, 2>(a, n_items, stream, ev_start, ev_stop);
   }
   return hipGetLastError();
 }

@@ -549,13 +549,9 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (plan->ev_before && (e = hipEventRecord(plan->ev_before, st)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
   e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, (plan->rows_stride + 15) / 16,
-                       plan->occ, st);
+                       plan->occ, st, plan->ev_before, plan->ev_after);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
-  if (plan->ev_after && (e = hipEventRecord(plan->ev_after, st)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
   if (!plan->red1.empty()) {
     // Two-level merge: chunks of the partials into first-level partials,
     // then the pairs' merge over those.
