@@ -288,6 +288,45 @@ def test_two_level_merge(name):
           partition_tokens=16)
 
 
+# A seeded sweep over random shapes: head dim and KV dtype, GQA group and
+# KV heads, ragged query lengths (padded slots included), contexts from the
+# query length to a few thousand keys, windows, sinks (per sequence or for
+# all), output dtype and partition size, each against the oracle.
+def _random_case(rng):
+    D = int(rng.choice([64, 128, 256]))
+    kv = "fp8" if D == 256 else str(rng.choice(["bf16", "fp8"]))
+    Hkv = int(rng.choice([1, 2]))
+    max_rows = 48 if D == 256 else 64
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g <= max_rows]))
+    qmax = min(8, max_rows // G)
+    B = int(rng.integers(1, 7))
+    q = [int(rng.integers(0, qmax + 1)) for _ in range(B)]
+    if max(q) == 0:
+        q[0] = 1
+    ctx = [max(qb, 1) + int(rng.integers(0, 3000)) for qb in q]
+    kw = dict(head_dim=D, kv_dtype=kv, num_q_heads=G * Hkv, num_kv_heads=Hkv, ctx_lens=ctx,
+              q_lens=q, out_dtype=str(rng.choice(["fp32", "bf16"])))
+    if rng.random() < 0.4:
+        kw["window"] = [int(rng.choice([0, 1, 7, 64, 500])) for _ in range(B)]
+    sinks = rng.integers(0, 3)
+    if sinks == 1:
+        kw["sinks_all"] = True
+    elif sinks == 2:
+        kw["sinks_rows"] = [bool(rng.random() < 0.5) for _ in range(B)]
+    P = rng.choice([0, 16, 32, 64, 256, 4096])
+    return kw, (None if P == 0 else int(P))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_sweep(case):
+    rng = np.random.default_rng(90_000 + case)
+    kw, P = _random_case(rng)
+    wl = edge(f"random sweep {case}", seed=90_000 + case, **kw)
+    check(wl, f"random sweep {case}: D={kw['head_dim']} {kw['kv_dtype']} "
+              f"G={kw['num_q_heads'] // kw['num_kv_heads']} Hkv={kw['num_kv_heads']}",
+          partition_tokens=P)
+
+
 def test_split_invariance():
     """The partitioning is a re-association of one sum: any split agrees."""
     wl = workloads.make(2, scale_ctx=1 / 8, num_seqs=3, out_dtype="fp32")
