@@ -321,7 +321,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path would shard by KV head, sequence or context; see DESIGN.md)",
+              "(the path would shard by KV head, by sequence or by context)",
               file=sys.stderr)
         sys.exit(2)
 
