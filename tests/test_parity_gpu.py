@@ -377,10 +377,9 @@ def test_repeat_calls_are_identical():
     pav.pa_free(plan)
 
 
-def test_graph_capture_replays_match_eager():
-    wl = workloads.make(2, scale_ctx=1 / 16, num_seqs=4)
+def _graph_replays_match_eager(wl, P):
     dev = wl.to("cuda:0")
-    plan = pav.plan_for(dev, device=0, partition_tokens=256)
+    plan = pav.plan_for(dev, device=0, partition_tokens=P)
     eager = pav.run(plan, dev)
     torch.cuda.synchronize()
     out = torch.empty_like(eager)
@@ -399,3 +398,22 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"graph replay {rep} differs from eager"
     pav.pa_free(plan)
+
+
+def test_graph_capture_replays_match_eager():
+    _graph_replays_match_eager(workloads.make(2, scale_ctx=1 / 16, num_seqs=4), 256)
+
+
+# The paths with more launches or other layouts under capture: two
+# workgroups per CU with the two-level merge (three launches), and FP8 many
+# split pairs (the row-block reduce).
+def test_graph_capture_two_level_and_row_block_reduce():
+    say("[gpu] graph capture: two-level merge, bf16, 16-key items")
+    _graph_replays_match_eager(
+        edge("graph two-level", **TWO_LEVEL["head dim 64, bf16, sinks"]), 16)
+    say("[gpu] graph capture: FP8 many split pairs")
+    kw = dict(MANY_PAIRS["head dim 128, FP8, windows and sinks"])
+    B, qs = kw.pop("B"), kw.pop("qs")
+    kw.pop("windowed")
+    ctx, q = _many_pairs(B, 11 + B, qs)
+    _graph_replays_match_eager(edge("graph many pairs", ctx_lens=ctx, q_lens=q, **kw), 32)
