@@ -86,11 +86,15 @@ def run_dev(plan, dev, lens_dev, out=None, stream=None):
     return out
 
 
-@pytest.mark.parametrize("config,P", [(2, None), (2, 64), (3, None), (5, None), (5, 128)])
+# (4, 16): one 64Ki-key sequence in 16-key items, 4,096 partials per (sequence,
+# KV head): two workgroups per CU and the two-level merge, with the items the
+# shorter length leaves empty folded through its first level.
+@pytest.mark.parametrize("config,P", [(2, None), (2, 64), (3, None), (5, None), (5, 128),
+                                      (4, 16)])
 def test_device_lengths_match_oracle(config, P):
     # not poisoned: a shorter length moves a window back over slots that the
     # bounds leave unread
-    wl = workloads.make(config, scale_ctx=1 / 16, num_seqs=12 if config != 2 else None,
+    wl = workloads.make(config, scale_ctx=1 / 16, num_seqs=12 if config not in (2, 4) else None,
                         poison=False)
     lens = shorter(wl, 100 + config)
     say(f"[gpu] device lengths: workload {config} P={P} bounds={wl.ctx_lens.tolist()[:6]} "
