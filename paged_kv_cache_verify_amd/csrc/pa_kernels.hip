@@ -478,13 +478,19 @@ __device__ __forceinline__ void mask_scores(const WaveState<D, FP8>& S, f32x4 (&
 template <bool FP8>
 constexpr float kShift = FP8 ? 6.0f : 0.0f;
 
-// The chunk's largest x per row (plus `extra`), and whether any row must move
-// its reference.
+// Whether any row must move its reference, and then (in mx) the chunk's
+// largest x per row, plus `extra`.
 template <int D, bool FP8>
 __device__ __forceinline__ bool needs_rescale(const WaveState<D, FP8>& S, const f32x4 (&sc)[2],
                                               float scale_log2, float extra, float& mx) {
-  mx = xlane_max4(max8(sc)) * scale_log2 + extra;
-  return __any(mx > S.m + (kShift<FP8> + kRescale));
+  // Some row must move exactly when some lane's own largest x exceeds the
+  // threshold (scale_log2 > 0, and the row's reference is the same on its
+  // four lanes), so the maximum across the row's lanes is only taken on
+  // that rare path.
+  mx = max8(sc) * scale_log2 + extra;
+  const bool move = __any(mx > S.m + (kShift<FP8> + kRescale));
+  if (move) mx = xlane_max4(mx);
+  return move;
 }
 
 template <int D, bool FP8>
