@@ -82,7 +82,7 @@ typedef enum { PA_BF16 = 0, PA_FP8_E4M3 = 1, PA_FP32 = 2 } pa_dtype;
 /* Limits (a shape beyond them is refused with PA_E_UNSUPPORTED). */
 #define PA_BLOCK_TOKENS 16      /* tokens per KV block */
 #define PA_MAX_QUERY_LEN 8      /* q_b <= 8: verify of 7 drafts + 1 */
-#define PA_MAX_ROWS 64          /* q_b x G <= 64 packed rows per KV head */
+#define PA_MAX_ROWS 128         /* q_b x G <= 128 packed rows per KV head */
 #define PA_MAX_CONTEXT 1048576  /* L_b <= 1 Mi tokens */
 #define PA_MAX_ITEM_KEYS 8192   /* partition_tokens <= 8192 */
 
@@ -90,7 +90,8 @@ typedef struct {
   int32_t num_seqs;           /* B >= 1 */
   int32_t num_q_heads;        /* Hq >= 1 */
   int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
-  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t head_dim;           /* D: 64 or 128 (bf16 or FP8 KV), or 256
+                                 (FP8 KV only) */
   int32_t block_size;         /* must be 16 (explicit: never defaulted) */
   int32_t num_blocks;         /* pool capacity, >= 1 */
   int32_t max_blocks_per_seq; /* block-table row stride in entries, >= 1 */
@@ -196,9 +197,14 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
  * lies outside [0, num_blocks) is skipped, so no table can make the call
  * store outside the pool. Enqueued on `stream` of the plan's device;
  * asynchronous, allocation-free and graph-capturable like pa_decode_verify.
+ * Served at every (head_dim, KV dtype) pa_plan accepts: 64 and 128 with
+ * bf16 or FP8 KV, 256 with FP8 KV. The new tokens' positions come from the
+ * plan's context lengths, so the plan must hold the step's actual lengths.
  * Returns PA_E_INVALID for a missing pointer, scales given for bf16 KV or
- * missing for FP8 KV, k_new/v_new/k_pool/v_pool not 4-byte aligned, or a
- * host-only plan (nothing is launched then), PA_E_HIP if the launch fails.
+ * missing for FP8 KV, k_new/v_new/k_pool/v_pool not 4-byte aligned (8-byte
+ * at head_dim 256), a plan built with lengths_are_bounds = 1, or a host-only
+ * plan; PA_E_UNSUPPORTED for a (head_dim, KV dtype) without an append
+ * kernel; PA_E_HIP if the launch fails. Nothing is launched on an error.
  * A plan whose sequences bring no new token returns PA_OK at once.
  */
 pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,
@@ -257,9 +263,12 @@ pa_status pa_plan_info(const pa_plan_t* plan, int64_t* kv_bytes,
                        int32_t* partition_tokens);
 
 /*
- * Copy the plan's work list to host memory as rows of 5 int32:
- * (sequence, kv head, first key, end key, partial slot or -1 when the item is
- * the only one of its (sequence, kv head) and writes the output directly).
+ * Copy the plan's work list to host memory as rows of 7 int32:
+ * (sequence, kv head, first key, end key, partial slot or -1 when the item
+ * covers all of its (sequence, kv head)'s keys and writes the output
+ * directly, first packed row, packed rows). A workgroup carries at most 64
+ * packed rows (48 at head_dim 256); a sequence with more is split into row
+ * blocks, each an item of its own over the same keys and slot.
  * Writes min(capacity, work_items) rows; returns PA_E_INVALID if items is
  * NULL while capacity > 0.
  */

@@ -19,6 +19,7 @@ LIBRARY = os.path.join(_HERE, "libpa_verify.so")
 
 PA_OK, PA_E_INVALID, PA_E_UNSUPPORTED, PA_E_HIP, PA_E_NOMEM = 0, 1, 2, 3, 4
 PA_BF16, PA_FP8_E4M3, PA_FP32 = 0, 1, 2
+ITEM_FIELDS = 7  # int32 per work item from pa_plan_items
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
 EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_kv_append",
@@ -147,10 +148,12 @@ class Plan:
                 "partition_tokens": p.value}
 
     def items(self):
+        """The work list: (sequence, kv head, first key, end key, slot,
+        first packed row, packed rows) per item."""
         n = self.info()["work_items"]
-        buf = (ctypes.c_int32 * (5 * max(n, 1)))()
+        buf = (ctypes.c_int32 * (ITEM_FIELDS * max(n, 1)))()
         _check(library().pa_plan_items(self.handle, buf, n))
-        return [tuple(buf[5 * i:5 * i + 5]) for i in range(n)]
+        return [tuple(buf[ITEM_FIELDS * i:ITEM_FIELDS * (i + 1)]) for i in range(n)]
 
 
 def pa_plan(shape: PaShape, context_lens: Sequence[int], query_lens: Sequence[int],

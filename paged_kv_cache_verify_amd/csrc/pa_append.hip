@@ -3,8 +3,8 @@
 // attention kernels read them.
 //
 // One wave per stored row (one token, one KV head, K or V): the wave loads
-// the D bf16 values (D / 64 per lane), and either copies them bit for bit
-// (bf16 pool) or quantises them to e4m3 with the row's own fp32 scale,
+// the D bf16 values (D / 64 per lane: one, two or four), and either copies
+// them bit for bit (bf16 pool) or quantises them to e4m3 with the row's own fp32 scale,
 // scale = amax / 448 (the e4m3 maximum), code = nearest e4m3 value to
 // x / scale, ties to the even code. The amax is a wave reduction; lane 0
 // writes the scale.
@@ -59,20 +59,29 @@ __global__ __launch_bounds__(64 * kAppendRowsPerBlock) void pa_append_kernel(App
   const int64_t dst = ((int64_t)page * A.num_kv_heads + g) * kBlock + pos % kBlock;
   const uint16_t* src = (is_v ? A.v_new : A.k_new) + r * D + lane * E;
 
-  uint32_t bits;  // E bf16 values, the first in the low half
-  if constexpr (E == 2) bits = *reinterpret_cast<const uint32_t*>(src);
-  else bits = *src;
+  // E bf16 values, the first in the low half of word 0.
+  uint32_t bits[(E + 1) / 2];
+  if constexpr (E == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src);
+    bits[0] = v.x;
+    bits[1] = v.y;
+  } else if constexpr (E == 2) {
+    bits[0] = *reinterpret_cast<const uint32_t*>(src);
+  } else {
+    bits[0] = *src;
+  }
 
   if constexpr (!FP8) {
     uint16_t* out = static_cast<uint16_t*>(is_v ? A.v_pool : A.k_pool) + dst * D + lane * E;
-    if constexpr (E == 2) *reinterpret_cast<uint32_t*>(out) = bits;
-    else *out = (uint16_t)bits;
+    if constexpr (E == 4) *reinterpret_cast<uint2*>(out) = make_uint2(bits[0], bits[1]);
+    else if constexpr (E == 2) *reinterpret_cast<uint32_t*>(out) = bits[0];
+    else *out = (uint16_t)bits[0];
   } else {
     float x[E];
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      x[e] = __uint_as_float(((bits >> (16 * e)) & 0xFFFFu) << 16);
+      x[e] = __uint_as_float(((bits[e / 2] >> (16 * (e % 2))) & 0xFFFFu) << 16);
       amax = fmaxf(amax, fabsf(x[e]));
     }
 #pragma unroll
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(64 * kAppendRowsPerBlock) void pa_append_kernel(App
       codes |= e4m3_rne(y) << (8 * e);
     }
     uint8_t* out = static_cast<uint8_t*>(is_v ? A.v_pool : A.k_pool) + dst * D + lane * E;
-    if constexpr (E == 2) *reinterpret_cast<uint16_t*>(out) = (uint16_t)codes;
+    if constexpr (E == 4) *reinterpret_cast<uint32_t*>(out) = codes;
+    else if constexpr (E == 2) *reinterpret_cast<uint16_t*>(out) = (uint16_t)codes;
     else *out = (uint8_t)codes;
     if (lane == 0) (is_v ? A.v_scales : A.k_scales)[dst] = scale;
   }
@@ -98,12 +108,19 @@ hipError_t launch_append(const AppendArgs& a, int head_dim, bool fp8, hipStream_
   if (rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)((rows + kAppendRowsPerBlock - 1) / kAppendRowsPerBlock));
   const dim3 block(64 * kAppendRowsPerBlock);
-  if (head_dim == 128) {
+  // One instance per head dim the attention serves (head 256 with FP8 KV
+  // only); any other combination is refused here, before a launch.
+  if (head_dim == 256) {
+    if (!fp8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_append_kernel<256, true>), grid, block, 0, stream, a);
+  } else if (head_dim == 128) {
     if (fp8) hipLaunchKernelGGL((pa_append_kernel<128, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((pa_append_kernel<128, false>), grid, block, 0, stream, a);
-  } else {
+  } else if (head_dim == 64) {
     if (fp8) hipLaunchKernelGGL((pa_append_kernel<64, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((pa_append_kernel<64, false>), grid, block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -9,8 +9,12 @@ namespace pav {
 
 constexpr int kBlock = 16;      // tokens per KV block
 constexpr int kChunk = 32;      // tokens a wave consumes per iteration (two blocks)
-constexpr int kMaxRows = 64;    // q x G packed rows per KV head (4 MFMA row tiles)
-constexpr int kMaxRows256 = 48; // ... at head_dim 256 (3 row tiles)
+constexpr int kMaxRows = 128;      // q x G packed rows per KV head
+// Rows one partition workgroup carries: 4 MFMA row tiles, 3 at head_dim 256.
+// A sequence with more rows is split into row blocks of at most this many,
+// each a work item of its own over the same keys.
+constexpr int kItemRows = 64;
+constexpr int kItemRows256 = 48;
 constexpr int kMaxQuery = 8;
 constexpr int kMaxContext = 1 << 20;
 // Keys a work item spans from its page-aligned start; the workgroup keeps
@@ -35,7 +39,10 @@ struct WorkItem {
   int32_t q_len;
   int32_t q_off;
   int32_t window;
-  int32_t pad[7];
+  // the item's packed rows: [row0, row0 + nrows) of the q x G rows
+  int32_t row0;
+  int32_t nrows;
+  int32_t pad[5];
 };
 
 // A split (sequence, KV head) whose partials [slot_base, slot_base +

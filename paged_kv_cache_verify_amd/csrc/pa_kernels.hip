@@ -472,9 +472,9 @@ __device__ __forceinline__ void mask_scores(const WaveState<D, FP8>& S, f32x4 (&
 // probabilities to l and returns p w per score element, w the token's V scale
 // (FP8) or 1.
 //
-// FP8: `extra` (>= 0, log2 units) raises the chunk's largest x for that test,
-// so that a chunk whose V scales reach 2^(1 + extra) still keeps p w below
-// 2^15.
+// FP8: `extra` (log2 units, per lane) raises the lane's largest x for that
+// test by the log2 bound of its V scales minus one, so the bounds hold for
+// p w rather than p: p w stays below 2^15 whatever the scales are.
 template <bool FP8>
 constexpr float kShift = FP8 ? 6.0f : 0.0f;
 
@@ -809,17 +809,16 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
       }
     }
   }
-  // p w enters an fp16 product: p < 2^14 keeps it below 2^15 while the V
-  // scales stay at most 2; a chunk with a larger V scale w raises the
-  // softmax reference by log2(w) - 1 (rare: |V| above 896).
-  float extra = 0.f;
-  {
-    const float vmax = max8(X.vs);
-    if (__any(vmax > 2.0f)) {
-      asm volatile("");  // a real branch
-      extra = __builtin_amdgcn_logf(xlane_max4(vmax)) - 1.0f;
-    }
-  }
+  // p w enters an fp16 product, so the reference is kept for p w rather
+  // than for p: each lane raises its chunk maximum of x by e - 1, where
+  // 2^(e-1) <= its largest V scale < 2^e (e from the exponent, at least
+  // -63). After a rescale a row's largest p w is then within [2^6, 2^7], and
+  // no chunk reaches 2^15 before the next one, whatever the magnitude of the
+  // scales: V scales far below 1 keep p w clear of fp16's subnormal range,
+  // and large ones of its overflow. (p itself stays below 2^78, l below
+  // 2^98 over 1 Mi keys: far inside fp32.)
+  const float vmax = max8(X.vs);
+  const float extra = (float)(max(__builtin_amdgcn_frexp_expf(vmax), -63) - 1);
   return needs_rescale(S, X.sc, scale_log2, extra, X.mx);
 }
 
@@ -985,7 +984,11 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
     tv0 = max(tv0, lo);
     tv1 = min(tv1, L);
   }
-  const int rows = q * G;
+  // The item's packed rows: [row0, row0 + rows) of the sequence's q x G
+  // (a sequence with more rows than a workgroup carries is split into row
+  // blocks, each its own item over the same keys).
+  const int row0 = it.row0;
+  const int rows = it.nrows;
   const int nt = (rows + 15) >> 4;  // row tiles; waves r >= nt do not compute
   const bool active = r < nt;
   const int tokbase = (tv0 >> 4) << 4;
@@ -1036,8 +1039,8 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
     sm.pages[i] = bt[(which == 0 || tok0 + kBlock < tv1) ? pg : pg - 1];
   }
 
-  // The wave's row tile: row = 16 r + lane % 16 (padding rows mirror the
-  // last real row and carry a zero query).
+  // The wave's row tile: item row 16 r + lane % 16, packed row row0 + that
+  // (padding rows mirror the item's last row and carry a zero query).
   WaveState<D, FP8> S;
   S.m = -INFINITY;
   S.l = 0.f;
@@ -1049,7 +1052,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   if (!loader) {
     const int row = 16 * r + n;
     const bool live = active && row < rows;
-    const int rr = live ? row : rows - 1;
+    const int rr = row0 + (live ? row : rows - 1);
     const int i = rr / G, hh = rr % G;
     S.prow = L - q + i;
     const uint16_t* qp = A.q + ((int64_t)(it.q_off + i) * Hq + g * G + hh) * D;
@@ -1167,7 +1170,8 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   // ---- Epilogue: the wave writes its rows (lane: row n, d = 16 mt + 4 c + i).
   const int row = 16 * r + n;
   if (row >= rows) return;
-  const int i = row / G, hh = row % G;
+  const int arow = row0 + row;  // packed row within the sequence's q x G
+  const int i = arow / G, hh = arow % G;
   const int h = g * G + hh;
   if (it.slot < 0) {
     const float zs = sink_log2(A, b, h);
@@ -1183,7 +1187,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
     // once, and lines kept out of the L2 make the kernel's final write-back
     // shorter (the partition kernel measured 1.5 us faster on the MTP-5
     // workload).
-    const int64_t pr = (int64_t)it.slot * A.rows_stride + row;
+    const int64_t pr = (int64_t)it.slot * A.rows_stride + arow;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
       __builtin_nontemporal_store(S.o[mt],

@@ -36,7 +36,9 @@ struct SeqInfo {
   int32_t n_parts;   // work items per KV head
   int32_t piece;     // keys per work item (the last one may be shorter)
   int32_t slot_base; // partial slot of (kv head 0, part 0) when n_parts > 1
-  double cost;       // relative time per key of this sequence's items
+  int32_t rblocks;   // row blocks (work items per key piece)
+  int32_t rper;      // rows per row block (the last may have fewer)
+  double cost;       // relative time per key of one of this sequence's items
 };
 
 }  // namespace
@@ -55,6 +57,7 @@ struct pa_plan_s {
   std::vector<ReduceItem> red;  // split (sequence, KV head) pairs
   int32_t max_parts = 0;        // most partials of any split pair
   int32_t occ = 1;              // partition workgroups per CU (2 when items exceed one round)
+  int32_t ntmax = 1;            // row tiles of the largest item (selects the kernel layout)
   std::vector<int32_t> tokens;  // [T][2]: sequence, position of each new token
   std::vector<int32_t> seq_rows;  // [B][2]: first verify row, verify rows (q)
   WorkItem* d_items = nullptr;
@@ -80,6 +83,8 @@ struct pa_plan_s {
 namespace {
 
 thread_local std::string g_last_error;
+
+constexpr int kItemFields = 7;  // int32 per row of pa_plan_items
 
 pa_status fail(pa_status st, const char* fmt, ...) {
   char buf[512];
@@ -185,11 +190,10 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
       return fail(PA_E_INVALID, "context_lens[%d] = %d needs more blocks than the pool holds", b,
                   L);
     if (win && win[b] < 0) return fail(PA_E_INVALID, "window[%d] = %d < 0", b, win[b]);
-    const int max_rows = s->head_dim == 256 ? kMaxRows256 : kMaxRows;
-    if (q * G > max_rows)
+    if (q * G > kMaxRows)
       return fail(PA_E_UNSUPPORTED,
-                  "sequence %d packs %d x %d = %d rows per KV head; at most %d are served at "
-                  "head_dim %d", b, q, G, q * G, max_rows, s->head_dim);
+                  "sequence %d packs %d x %d = %d rows per KV head; at most %d are served", b,
+                  q, G, q * G, kMaxRows);
     total_q += q;
   }
   if (total_q * s->num_q_heads * (int64_t)s->head_dim > ((int64_t)1 << 40))
@@ -227,7 +231,7 @@ int64_t count_items(const std::vector<SeqInfo>& seqs, int Hkv, double P, int64_t
     if (si.q_len == 0) continue;
     const int64_t span = si.ctx_len - (si.lo / kBlock) * kBlock;
     const int64_t piece = keys_for(P, si.cost, lo_keys);
-    n += Hkv * ((span + piece - 1) / piece);
+    n += (int64_t)Hkv * si.rblocks * ((span + piece - 1) / piece);
   }
   return n;
 }
@@ -243,7 +247,7 @@ double auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus, int64_t& l
   double total = 0.0, max_cost = 1.0;
   for (const SeqInfo& si : seqs)
     if (si.q_len > 0) {
-      total += (double)Hkv * (si.ctx_len - (si.lo / kBlock) * kBlock) * si.cost;
+      total += (double)Hkv * si.rblocks * (si.ctx_len - (si.lo / kBlock) * kBlock) * si.cost;
       max_cost = std::max(max_cost, si.cost);
     }
   lo_keys = kChunk;
@@ -313,6 +317,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       si.n_parts = 0;
       si.piece = 0;
       si.slot_base = -1;
+      si.rblocks = 0;
+      si.rper = 0;
       p->seq_rows.push_back(q_off);
       p->seq_rows.push_back(si.q_len);
       q_off += si.q_len;
@@ -328,14 +334,30 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     p->rows_stride = rows_stride;
     p->kv_bytes = total_keys * tok_bytes;
 
+    // Row blocks: a workgroup carries at most item_rows packed rows, so a
+    // sequence with more is split into ceil(rows / item_rows) blocks of
+    // about equal size (whole 16-row tiles), each a work item of its own
+    // over the same keys. They share the key piece's partial slot, each
+    // writing its own rows of it.
+    const int item_rows = s.head_dim == 256 ? kItemRows256 : kItemRows;
+    int max_item_rows = 0;
+    for (SeqInfo& si : p->seqs) {
+      if (si.q_len == 0) continue;
+      const int rows = si.q_len * G;
+      si.rblocks = (rows + item_rows - 1) / item_rows;
+      si.rper = (((rows + si.rblocks - 1) / si.rblocks) + 15) / 16 * 16;
+      si.rper = std::min(si.rper, rows);
+      max_item_rows = std::max(max_item_rows, si.rper);
+    }
+    p->ntmax = (max_item_rows + 15) / 16;
     // Cut [a, L) of every active sequence, a = lo rounded down to a page,
     // into pieces of one size per sequence (a multiple of 16 keys, so every
     // cut falls on a page boundary), the same for every KV head. A caller's
     // partition_tokens is that size for every sequence; otherwise each
     // sequence is cut into as few equal pieces of at most the plan's item
     // size as will do.
-    const int ntmax = (rows_stride + 15) / 16;
-    for (SeqInfo& si : p->seqs) si.cost = item_cost(s, si.q_len * G, ntmax);
+    const int ntmax = p->ntmax;
+    for (SeqInfo& si : p->seqs) si.cost = item_cost(s, si.rper, ntmax);
     int64_t lo_keys = kChunk;
     const double weighted = s.partition_tokens > 0 ? 0.0 : auto_piece(p->seqs, Hkv, cus, lo_keys);
     int64_t slots = 0;
@@ -362,17 +384,22 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       }
       for (int g = 0; g < Hkv; ++g) {
         for (int k = 0; k < si.n_parts; ++k) {
-          WorkItem it{};
-          it.seq = b;
-          it.kv_head = g;
-          it.key_begin = std::max(si.lo, a + k * si.piece);
-          it.key_end = std::min(si.ctx_len, a + (k + 1) * si.piece);
-          it.slot = si.n_parts > 1 ? (int32_t)(si.slot_base + (int64_t)g * si.n_parts + k) : -1;
-          it.ctx_len = si.ctx_len;
-          it.q_len = si.q_len;
-          it.q_off = si.q_off;
-          it.window = si.window;
-          p->items.push_back(it);
+          for (int rb = 0; rb < si.rblocks; ++rb) {
+            WorkItem it{};
+            it.seq = b;
+            it.kv_head = g;
+            it.key_begin = std::max(si.lo, a + k * si.piece);
+            it.key_end = std::min(si.ctx_len, a + (k + 1) * si.piece);
+            it.slot =
+                si.n_parts > 1 ? (int32_t)(si.slot_base + (int64_t)g * si.n_parts + k) : -1;
+            it.ctx_len = si.ctx_len;
+            it.q_len = si.q_len;
+            it.q_off = si.q_off;
+            it.window = si.window;
+            it.row0 = rb * si.rper;
+            it.nrows = std::min(si.rper, si.q_len * G - it.row0);
+            p->items.push_back(it);
+          }
         }
         if (si.n_parts > 1) {
           ReduceItem r{};
@@ -549,8 +576,8 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, (plan->rows_stride + 15) / 16,
-                       plan->occ, st, plan->ev_before, plan->ev_after);
+  e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, plan->ntmax, plan->occ, st,
+                       plan->ev_before, plan->ev_after);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (!plan->red1.empty()) {
     // Two-level merge: chunks of the partials into first-level partials,
@@ -599,18 +626,33 @@ pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_n
                        const int32_t* block_table, void* k_pool, void* v_pool,
                        float* k_scales, float* v_scales, void* stream) {
   if (!plan) return fail(PA_E_INVALID, "plan is NULL");
-  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
   const pa_shape& s = plan->shape;
   const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
+  // The append kernel has one instance per served (head dim, KV dtype):
+  // 64 and 128 with either KV dtype, 256 with FP8 KV (what validate()
+  // accepts). Anything else is refused here, never run on another instance.
+  if (!((s.head_dim == 64 || s.head_dim == 128) || (s.head_dim == 256 && fp8)))
+    return fail(PA_E_UNSUPPORTED, "no KV append for head_dim %d with %s KV", s.head_dim,
+                fp8 ? "FP8" : "bf16");
+  // The new tokens' positions come from the plan's lengths; on a plan built
+  // on upper bounds those are not the lengths a device-length call reads.
+  if (s.lengths_are_bounds)
+    return fail(PA_E_INVALID,
+                "a plan built on upper bounds (lengths_are_bounds = 1) has no new-token "
+                "positions: plan the append with the step's actual lengths");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
   if (plan->tokens.empty()) return PA_OK;  // no sequence brings a new token
   if (!k_new || !v_new || !block_table || !k_pool || !v_pool)
     return fail(PA_E_INVALID, "k_new, v_new, block_table, k_pool and v_pool are required");
   if (fp8 && (!k_scales || !v_scales))
     return fail(PA_E_INVALID, "FP8 KV needs k_scales and v_scales");
   if (!fp8 && (k_scales || v_scales)) return fail(PA_E_INVALID, "bf16 KV takes no scales");
+  // Each lane moves D / 64 values: 8 bytes of bf16 input at head dim 256.
+  const uintptr_t align = s.head_dim == 256 ? 8 : 4;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
-       reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 3)
-    return fail(PA_E_INVALID, "k_new, v_new, k_pool and v_pool must be 4-byte aligned");
+       reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & (align - 1))
+    return fail(PA_E_INVALID, "k_new, v_new, k_pool and v_pool must be %d-byte aligned",
+                (int)align);
 
   AppendArgs a{};
   a.k_new = static_cast<const uint16_t*>(k_new);
@@ -694,11 +736,14 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
   const int32_t n = std::min<int32_t>(capacity, (int32_t)plan->items.size());
   for (int32_t i = 0; i < n; ++i) {
     const WorkItem& it = plan->items[i];
-    items[5 * i + 0] = it.seq;
-    items[5 * i + 1] = it.kv_head;
-    items[5 * i + 2] = it.key_begin;
-    items[5 * i + 3] = it.key_end;
-    items[5 * i + 4] = it.slot;
+    int32_t* r = items + (int64_t)kItemFields * i;
+    r[0] = it.seq;
+    r[1] = it.kv_head;
+    r[2] = it.key_begin;
+    r[3] = it.key_end;
+    r[4] = it.slot;
+    r[5] = it.row0;
+    r[6] = it.nrows;
   }
   return PA_OK;
 }

@@ -66,8 +66,8 @@ REFUSALS = [
     (dict(block_size=32), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "block_size"),
     (dict(head_dim=96), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "head_dim"),
     (dict(head_dim=256), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "FP8"),
-    (dict(head_dim=256, kv_dtype="fp8", num_q_heads=16, num_kv_heads=2), [100, 50], [8, 6],
-     None, pav.PA_E_UNSUPPORTED, "at most 48"),
+    (dict(head_dim=256, kv_dtype="fp8", num_q_heads=34, num_kv_heads=2), [100, 50], [8, 6],
+     None, pav.PA_E_UNSUPPORTED, "at most 128"),
     (dict(num_q_heads=15), [100, 50], [6, 6], None, pav.PA_E_INVALID, "multiple"),
     (dict(num_seqs=0), [], [], None, pav.PA_E_INVALID, "num_seqs"),
     (dict(kv_dtype="fp32"), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED, "kv_dtype"),
@@ -88,9 +88,9 @@ REFUSALS = [
     (dict(max_blocks_per_seq=4), [100, 50], [6, 6], None, pav.PA_E_INVALID, "max_blocks"),
     (dict(num_blocks=3), [100, 50], [6, 6], None, pav.PA_E_INVALID, "pool"),
     ({}, [100, 50], [6, 6], [-1, 0], pav.PA_E_INVALID, "window"),
-    (dict(num_q_heads=32, num_kv_heads=2), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED,
+    (dict(num_q_heads=48, num_kv_heads=2), [100, 50], [6, 6], None, pav.PA_E_UNSUPPORTED,
      "rows"),
-    (dict(num_q_heads=16, num_kv_heads=1), [100, 50], [5, 1], None, pav.PA_E_UNSUPPORTED,
+    (dict(num_q_heads=32, num_kv_heads=1), [100, 50], [5, 1], None, pav.PA_E_UNSUPPORTED,
      "rows"),
 ]
 
@@ -146,36 +146,47 @@ def test_host_only_plan_refuses_to_run():
     plan.close()
 
 
-def check_worklist(plan, ctx, q, win, Hkv, P=None):
-    """Items of every (sequence, kv head) tile its visible keys exactly once,
-    in page-aligned pieces; slots are unique; single items write directly."""
+def check_worklist(plan, ctx, q, win, Hkv, P=None, G=8, item_rows=64):
+    """Items of every (sequence, kv head, row block) tile its visible keys
+    exactly once, in page-aligned pieces; the row blocks of a sequence tile
+    its q x G packed rows, at most item_rows each; the row blocks of one key
+    piece share its slot and no two key pieces share one; single pieces
+    write directly."""
     items = plan.items()
     info = plan.info()
     assert info["work_items"] == len(items)
     P = P or info["partition_tokens"]
     per = {}
-    slots = set()
-    for (b, g, k0, k1, slot) in items:
+    slot_of = {}
+    for (b, g, k0, k1, slot, r0, nr) in items:
         assert 0 <= g < Hkv and k0 < k1 and (k1 - k0) <= P
-        per.setdefault((b, g), []).append((k0, k1, slot))
+        assert 0 < nr <= item_rows and r0 >= 0 and r0 + nr <= q[b] * G
+        per.setdefault((b, g, r0, nr), []).append((k0, k1, slot))
         if slot >= 0:
-            assert slot not in slots
-            slots.add(slot)
+            assert slot_of.setdefault(slot, (b, g, k0, k1)) == (b, g, k0, k1)
     for b, (L, qb) in enumerate(zip(ctx, q)):
         W = win[b] if win else 0
         for g in range(Hkv):
+            blocks = sorted((r0, nr) for (bb, gg, r0, nr) in per if (bb, gg) == (b, g))
             if qb == 0:
-                assert (b, g) not in per
+                assert not blocks
                 continue
+            assert blocks[0][0] == 0 and sum(nr for _, nr in blocks) == qb * G
+            for (r0, nr), (r1, _) in zip(blocks, blocks[1:]):
+                assert r0 + nr == r1
             lo = max(0, L - qb - W + 1) if W > 0 else 0
-            segs = sorted(per[(b, g)])
-            assert segs[0][0] == lo and segs[-1][1] == L
-            for (a0, a1, _), (b0, _, _) in zip(segs, segs[1:]):
-                assert a1 == b0 and a1 % 16 == 0
-            if len(segs) == 1:
-                assert segs[0][2] == -1
-            else:
-                assert all(s >= 0 for _, _, s in segs)
+            pieces = None
+            for blk in blocks:
+                segs = sorted(per[(b, g) + blk])
+                assert segs[0][0] == lo and segs[-1][1] == L
+                for (a0, a1, _), (b0, _, _) in zip(segs, segs[1:]):
+                    assert a1 == b0 and a1 % 16 == 0
+                if len(segs) == 1:
+                    assert segs[0][2] == -1
+                else:
+                    assert all(s >= 0 for _, _, s in segs)
+                assert pieces is None or pieces == segs  # one key cut, one slot per piece
+                pieces = segs
     return items
 
 
@@ -195,7 +206,8 @@ def test_worklist_for_named_workloads():
         wl = workloads.make(cfg, scale_ctx=0.25) if cfg != 1 else workloads.make(1)
         plan = pav.plan_for(wl, device=-1)
         win = None if wl.window is None else wl.window.tolist()
-        check_worklist(plan, wl.ctx_lens.tolist(), wl.q_lens.tolist(), win, wl.num_kv_heads)
+        check_worklist(plan, wl.ctx_lens.tolist(), wl.q_lens.tolist(), win, wl.num_kv_heads,
+                       G=wl.group)
         assert plan.info()["kv_bytes"] == wl.kv_bytes()
         plan.close()
 
@@ -219,7 +231,7 @@ def test_head256_worklist_at_full_size():
                        num_blocks=150000, max_blocks_per_seq=9375, softmax_scale=0.0625)
     ctx, q = [150000] * 8, [6] * 8
     plan = pav.pa_plan(shape, ctx, q, None, device=-1)
-    check_worklist(plan, ctx, q, None, 1)
+    check_worklist(plan, ctx, q, None, 1, item_rows=48)
     info = plan.info()
     assert info["kv_bytes"] == 8 * 150000 * (2 * 256 + 8)
     assert info["work_items"] <= 256  # one round of the device's CUs
@@ -260,10 +272,43 @@ def test_fp8_plan_weights_items_by_row_tiles():
         plan = pav.pa_plan(shape, ctx, q, None, device=-1)
         items = check_worklist(plan, ctx, q, None, 2)
         assert len(items) <= 256
-        longest = {qq: max(k1 - k0 for (b, _, k0, k1, _) in items if q[b] == qq) for qq in (2, 6)}
+        longest = {qq: max(it[3] - it[2] for it in items if q[it[0]] == qq) for qq in (2, 6)}
         if kv == "fp8":
             # weights 1 + (4/3)(tiles/4): 4/3 for one tile, 2 for three
             assert 1.3 < longest[2] / longest[6] < 1.7
         else:
             assert longest[2] == longest[6]
         plan.close()
+
+
+@pytest.mark.parametrize("D,kv,cap", [(128, "bf16", 64), (128, "fp8", 64), (64, "bf16", 64),
+                                      (256, "fp8", 48)])
+def test_rows_beyond_one_workgroup_are_split_into_row_blocks(D, kv, cap):
+    """Up to 128 packed rows per KV head (q 8 x group 16): a sequence with
+    more rows than a workgroup carries is cut into row blocks of whole 16-row
+    tiles, each an item over the same keys sharing the key piece's slot;
+    the kv_bytes figure counts the keys once."""
+    ctx, q = [5000, 700, 40, 3000], [8, 1, 5, 6]
+    G = 16
+    for P in (0, 512):
+        shape = base_shape(num_seqs=4, num_q_heads=2 * G, num_kv_heads=2, head_dim=D,
+                           kv_dtype=kv, partition_tokens=P)
+        plan = pav.pa_plan(shape, ctx, q, None, device=-1)
+        items = check_worklist(plan, ctx, q, None, 2, P or None, G=G, item_rows=cap)
+        blocks = sorted({(it[5], it[6]) for it in items if it[0] == 0})
+        want = {64: [(0, 64), (64, 64)], 48: [(0, 48), (48, 48), (96, 32)]}[cap]
+        assert blocks == want
+        assert sorted({(it[5], it[6]) for it in items if it[0] == 1}) == [(0, 16)]
+        per_tok = 2 * D * (1 if kv == "fp8" else 2) + (8 if kv == "fp8" else 0)
+        assert plan.info()["kv_bytes"] == 2 * sum(ctx) * per_tok
+        plan.close()
+
+
+def test_append_refusals_before_any_launch():
+    """pa_kv_append refuses a plan built on upper bounds (its new-token
+    positions would come from the bounds) before looking at any pointer."""
+    shape = base_shape(lengths_are_bounds=1)
+    plan = pav.pa_plan(shape, [100, 50], [6, 6], None, device=-1)
+    st = pav.library().pa_kv_append(plan.handle, 8, 8, 8, 8, 8, None, None, None)
+    assert st == pav.PA_E_INVALID and "upper bounds" in pav.pa_last_error()
+    plan.close()
