@@ -177,6 +177,31 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
                                void* stream);
 
 /*
+ * pa_decode_verify for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the call allocates nothing, and the plan may be a host-only
+ * one (pa_plan with device = -1, which owns no device memory either).
+ * The work list, the reduce lists and the partial results go into the
+ * library's static scratch, a device array of 64 MiB that every device the
+ * library runs on holds from the library's first use there until the
+ * process ends; the work lists are copied into it with hipMemcpyAsync on
+ * `stream` ahead of the kernels (so the plan must outlive the call's stream
+ * work). Runs on the current device (a device plan must be for it) with the
+ * plan's context lengths. Every call on a device shares that device's
+ * scratch: calls that overlap on one device (on different streams, or from
+ * different threads) race and must be serialised by the caller. Nothing in
+ * the scratch needs clearing: a call writes every value it reads.
+ * Returns PA_E_UNSUPPORTED, before any HIP call, when the plan's work list
+ * and partials exceed the scratch (e.g. a 1 Mi-token context cut into
+ * 512-key items: use pa_decode_verify or larger items); otherwise the
+ * errors of pa_decode_verify, with host-only plans accepted.
+ */
+pa_status pa_decode_verify_noalloc(const pa_plan_t* plan, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const float* k_scales, const float* v_scales,
+                                   const float* sinks, void* out, void* stream);
+
+/*
  * Paged KV append: write the plan's new tokens (the last q_b positions of
  * every sequence, L_b - q_b .. L_b - 1) into their 16-token slots, the step
  * before verify attention. Source: ATOM #3091 ("High-interactivity

@@ -145,4 +145,11 @@ hipError_t launch_reduce_stage1(const KernelArgs& a, int n_chunks, int head_dim,
                                 hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int head_dim, bool fp8, hipStream_t stream);
 
+// The zero-allocation attention call's scratch: a file-scope device array of
+// this many bytes (pa_noalloc.hip), one copy per device the library runs on.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Its device address on `device` (which must be the current device), looked
+// up once per device and cached.
+hipError_t noalloc_scratch(int device, void** ptr);
+
 }  // namespace pav

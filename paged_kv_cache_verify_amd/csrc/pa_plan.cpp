@@ -533,14 +533,24 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
 
 namespace {
 
-pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, const void* k_pool,
-                 const void* v_pool, const int32_t* block_table, const float* k_scales,
-                 const float* v_scales, const float* sinks, void* out, void* stream) {
-  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
-  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+// Device buffers one call uses: the plan's own, or the zero-allocation
+// call's carve-up of the library's static scratch.
+struct CallBufs {
+  const WorkItem* items;
+  const ReduceItem* red;
+  const ReduceItem* red1;
+  float* part_o;
+  float* part_ml;
+  float* l1_o;
+  float* l1_ml;
+};
+
+// The argument checks every attention call makes before it launches.
+pa_status check_call(const pa_plan_t* plan, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const float* k_scales, const float* v_scales,
+                     const float* sinks, void* out) {
   const pa_shape& s = plan->shape;
   const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
-  if (plan->items.empty()) return PA_OK;  // every sequence is a padded slot
   if (!q || !k_pool || !v_pool || !block_table || !out)
     return fail(PA_E_INVALID, "q, k_pool, v_pool, block_table and out are required");
   if (fp8 && (!k_scales || !v_scales))
@@ -550,7 +560,16 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   if (s.sinks_mode != 0 && !sinks) return fail(PA_E_INVALID, "sinks_mode %d needs sinks",
                                                s.sinks_mode);
   if (s.sinks_mode == 0 && sinks) return fail(PA_E_INVALID, "sinks given with sinks_mode 0");
+  return PA_OK;
+}
 
+// Enqueue the partition kernel and the reduce (one or two launches).
+pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* dev_ctx,
+                      const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const float* k_scales, const float* v_scales,
+                      const float* sinks, void* out, hipStream_t st) {
+  const pa_shape& s = plan->shape;
+  const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
   KernelArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_pool = k_pool;
@@ -560,10 +579,10 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   a.v_scales = v_scales;
   a.sinks = sinks;
   a.out = out;
-  a.part_o = plan->d_part_o;
-  a.part_ml = plan->d_part_ml;
-  a.items = plan->d_items;
-  a.red = plan->d_red;
+  a.part_o = d.part_o;
+  a.part_ml = d.part_ml;
+  a.items = d.items;
+  a.red = d.red;
   a.num_q_heads = s.num_q_heads;
   a.num_kv_heads = s.num_kv_heads;
   a.group = s.num_q_heads / s.num_kv_heads;
@@ -574,7 +593,6 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   a.scale_log2 = s.softmax_scale * kLog2e;
   a.dev_ctx = dev_ctx;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, plan->ntmax, plan->occ, st,
                        plan->ev_before, plan->ev_after);
@@ -582,18 +600,54 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   if (!plan->red1.empty()) {
     // Two-level merge: chunks of the partials into first-level partials,
     // then the pairs' merge over those.
-    a.red = plan->d_red1;
-    a.l1_o = plan->d_l1_o;
-    a.l1_ml = plan->d_l1_ml;
+    a.red = d.red1;
+    a.l1_o = d.l1_o;
+    a.l1_ml = d.l1_ml;
     e = launch_reduce_stage1(a, (int)plan->red1.size(), s.head_dim, plan->rows_stride, st);
     if (e != hipSuccess) return hip_fail(e, "first-level reduce kernel launch");
-    a.red = plan->d_red;
-    a.part_o = plan->d_l1_o;
-    a.part_ml = plan->d_l1_ml;
+    a.red = d.red;
+    a.part_o = d.l1_o;
+    a.part_ml = d.l1_ml;
   }
   e = launch_reduce(a, (int)plan->red.size(), s.head_dim, plan->rows_stride, plan->max_parts, st);
   if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   return PA_OK;
+}
+
+pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, const void* k_pool,
+                 const void* v_pool, const int32_t* block_table, const float* k_scales,
+                 const float* v_scales, const float* sinks, void* out, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+  if (plan->items.empty()) return PA_OK;  // every sequence is a padded slot
+  pa_status st = check_call(plan, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks, out);
+  if (st != PA_OK) return st;
+  const CallBufs d{plan->d_items, plan->d_red,  plan->d_red1, plan->d_part_o,
+                   plan->d_part_ml, plan->d_l1_o, plan->d_l1_ml};
+  return launch_call(plan, d, dev_ctx, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
+                     out, static_cast<hipStream_t>(stream));
+}
+
+// Byte offsets of one zero-allocation call's buffers in the static scratch
+// (each 256-byte aligned); `total` is what the call needs.
+struct StaticLayout {
+  size_t items, red, red1, part_o, part_ml, l1_o, l1_ml, total;
+};
+
+StaticLayout static_layout(const pa_plan_t* p) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t D = (size_t)p->shape.head_dim, R = (size_t)p->rows_stride;
+  StaticLayout L{};
+  size_t o = 0;
+  L.items = o; o += up(p->items.size() * sizeof(WorkItem));
+  L.red = o; o += up(p->red.size() * sizeof(ReduceItem));
+  L.red1 = o; o += up(p->red1.size() * sizeof(ReduceItem));
+  L.part_o = o; o += up((size_t)p->n_slots * R * D * sizeof(float));
+  L.part_ml = o; o += up((size_t)p->n_slots * R * 2 * sizeof(float));
+  L.l1_o = o; o += up((size_t)p->l1_slots * R * D * sizeof(float));
+  L.l1_ml = o; o += up((size_t)p->l1_slots * R * 2 * sizeof(float));
+  L.total = o;
+  return L;
 }
 
 }  // namespace
@@ -620,6 +674,50 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
                     "lengths_are_bounds = 1");
   return decode(plan, context_lens_dev, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
                 out, stream);
+}
+
+pa_status pa_decode_verify_noalloc(const pa_plan_t* plan, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table,
+                                   const float* k_scales, const float* v_scales,
+                                   const float* sinks, void* out, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->items.empty()) return PA_OK;  // every sequence is a padded slot
+  pa_status st = check_call(plan, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks, out);
+  if (st != PA_OK) return st;
+  const StaticLayout L = static_layout(plan);
+  if (L.total > kNoAllocScratchBytes)
+    return fail(PA_E_UNSUPPORTED,
+                "the call needs %zu bytes of work list and partials; the static scratch of the "
+                "zero-allocation call holds %zu (use pa_decode_verify, or larger work items)",
+                L.total, (size_t)kNoAllocScratchBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (plan->device >= 0 && plan->device != dev)
+    return fail(PA_E_INVALID, "the plan was built for device %d, the current device is %d",
+                plan->device, dev);
+  unsigned char* base = nullptr;
+  e = noalloc_scratch(dev, reinterpret_cast<void**>(&base));
+  if (e != hipSuccess) return hip_fail(e, "locating the static scratch");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // The work lists go in ahead of the kernels on the same stream.
+  auto put = [&](size_t off, const void* src, size_t bytes) -> hipError_t {
+    if (bytes == 0) return hipSuccess;
+    return hipMemcpyAsync(base + off, src, bytes, hipMemcpyHostToDevice, hs);
+  };
+  e = put(L.items, plan->items.data(), plan->items.size() * sizeof(WorkItem));
+  if (e == hipSuccess) e = put(L.red, plan->red.data(), plan->red.size() * sizeof(ReduceItem));
+  if (e == hipSuccess) e = put(L.red1, plan->red1.data(), plan->red1.size() * sizeof(ReduceItem));
+  if (e != hipSuccess) return hip_fail(e, "copying the work list into the static scratch");
+  const CallBufs d{reinterpret_cast<const WorkItem*>(base + L.items),
+                   reinterpret_cast<const ReduceItem*>(base + L.red),
+                   reinterpret_cast<const ReduceItem*>(base + L.red1),
+                   reinterpret_cast<float*>(base + L.part_o),
+                   reinterpret_cast<float*>(base + L.part_ml),
+                   reinterpret_cast<float*>(base + L.l1_o),
+                   reinterpret_cast<float*>(base + L.l1_ml)};
+  return launch_call(plan, d, nullptr, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
+                     out, hs);
 }
 
 pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,

@@ -312,3 +312,23 @@ def test_append_refusals_before_any_launch():
     st = pav.library().pa_kv_append(plan.handle, 8, 8, 8, 8, 8, None, None, None)
     assert st == pav.PA_E_INVALID and "upper bounds" in pav.pa_last_error()
     plan.close()
+
+
+def test_noalloc_refuses_a_plan_beyond_its_static_scratch():
+    """The zero-allocation call checks the plan's work list and partials
+    against its static scratch before any HIP call: a 1 Mi-token context in
+    512-key items (about 100 MB of partials) is refused with a message; a
+    plan with no work returns at once."""
+    shape = base_shape(num_seqs=1, max_blocks_per_seq=65536, num_blocks=131072,
+                       partition_tokens=512)
+    plan = pav.pa_plan(shape, [1 << 20], [6], None, device=-1)
+    st = pav.library().pa_decode_verify_noalloc(plan.handle, 8, 8, 8, 8, None, None, None, 8,
+                                                None)
+    assert st == pav.PA_E_UNSUPPORTED and "static scratch" in pav.pa_last_error()
+    plan.close()
+    plan = pav.pa_plan(base_shape(num_seqs=2), [10, 20], [0, 0], None, device=-1)
+    assert pav.library().pa_decode_verify_noalloc(plan.handle, None, None, None, None, None,
+                                                  None, None, None, None) == pav.PA_OK
+    plan.close()
+    assert pav.library().pa_decode_verify_noalloc(None, None, None, None, None, None, None,
+                                                  None, None, None) == pav.PA_E_INVALID
