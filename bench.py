@@ -172,9 +172,22 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None
     eager = time.perf_counter() - e0
     pav.pa_set_partition_events(plan, None, None)
     part_ms = [b.elapsed_time(a) for b, a in zip(ev_b, ev_a)]
+    # The streaming floor: the same plan's bytes through the same loads with
+    # no compute (pa_stream_floor), timed the same way on the same copies.
+    floor_ms = None
+    if lens_dev is None:
+        with torch.cuda.stream(s):
+            for i in range(steps):
+                kp, vp, ks, vs = pools[i % copies]
+                pav.pa_set_partition_events(plan, ev_b[i], ev_a[i])
+                pav.pa_stream_floor(plan, kp, vp, dev.block_table, ks, vs, s)
+        torch.cuda.synchronize()
+        pav.pa_set_partition_events(plan, None, None)
+        floor_ms = [b.elapsed_time(a) for b, a in zip(ev_b, ev_a)]
     del g
     pav.pa_free(plan)
     return {
+        "floor_ms_mean": None if floor_ms is None else statistics.fmean(floor_ms),
         "kv_bytes": kv,
         "copies": copies,
         "plan": info,
@@ -355,7 +368,8 @@ def main():
         f"{1e3 * r['event_ms_per_step']:.1f} us/step, partition kernel mean "
         f"{1e3 * r['partition_ms_mean']:.1f} us (median {1e3 * r['partition_ms_median']:.1f}, "
         f"p90 {1e3 * r['partition_ms_p90']:.1f}) = {achieved:.0f} GB/s, eager "
-        f"{1e3 * r['eager_ms_per_step']:.1f} us/step; plan {r['plan']}, {r['copies']} pool copies")
+        f"{1e3 * r['eager_ms_per_step']:.1f} us/step; stream floor {1e3 * r['floor_ms_mean']:.1f} us; "
+        f"plan {r['plan']}, {r['copies']} pool copies")
 
     key = f"workload{main_cfg}"
     line = {
@@ -395,6 +409,13 @@ def main():
             "partition_us_median": round(1e3 * r["partition_ms_median"], 2),
             "partition_us_p90": round(1e3 * r["partition_ms_p90"], 2),
         },
+        "stream_floor": {
+            "kernel": "pa_stream_floor_kernel (the plan's KV bytes, same loads, no compute)",
+            "us_mean": round(1e3 * r["floor_ms_mean"], 2),
+            "GB_s": round(r["kv_bytes"] / (r["floor_ms_mean"] * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(r["kv_bytes"] / (r["floor_ms_mean"] * 1e-3) / 1e9
+                                  / HBM_PEAK_GBS, 4),
+        },
     }
     if args.only is None:
         # The same calls on one pool copy: the KV stays in the Infinity Cache
@@ -414,13 +435,16 @@ def main():
             ach = rx["kv_bytes"] / (rx["partition_ms_mean"] * 1e-3) / 1e9
             log(f"  {1e3 * msx:.1f} us/call = {gbs:.0f} GB/s ({rx['mode']}); partition kernel "
                 f"{1e3 * rx['partition_ms_mean']:.1f} us = {ach:.0f} GB/s; eager "
-                f"{1e3 * rx['eager_ms_per_step']:.1f} us/call; plan {rx['plan']}")
+                f"{1e3 * rx['eager_ms_per_step']:.1f} us/call; stream floor "
+                f"{1e3 * rx['floor_ms_mean']:.1f} us; plan {rx['plan']}")
             extra[f"workload {cfg}" + ("" if P is None else f" (partition {P or 'auto'})")] = {
                 "us_per_call": round(1e3 * msx, 2),
                 "us_per_call_eager_launches": round(1e3 * rx["eager_ms_per_step"], 2),
                 "GB_s": round(gbs, 1),
                 "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                 "partition_kernel_GB_s": round(ach, 1),
+                "stream_floor_GB_s": round(rx["kv_bytes"] / (rx["floor_ms_mean"] * 1e-3) / 1e9,
+                                           1),
                 "kv_bytes_per_call": rx["kv_bytes"],
                 "work_items": rx["plan"]["work_items"],
                 "partition_tokens": rx["plan"]["partition_tokens"],
@@ -452,6 +476,8 @@ def main():
                 "GB_s": round(gbs, 1),
                 "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                 "partition_kernel_GB_s": round(ach, 1),
+                "stream_floor_GB_s": round(rx["kv_bytes"] / (rx["floor_ms_mean"] * 1e-3) / 1e9,
+                                           1),
                 "kv_bytes_per_call": rx["kv_bytes"],
                 "work_items": rx["plan"]["work_items"],
                 "pages_us_generic_kernel": pages_us[bs][0],

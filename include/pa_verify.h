@@ -266,6 +266,24 @@ pa_status pa_verify_greedy(const pa_plan_t* plan, const void* logits, pa_dtype l
                            int32_t* out_ids, int32_t* accepted, int32_t* next_ids,
                            void* stream);
 
+/*
+ * Measurement call: the streaming floor of a plan. One kernel reads exactly
+ * the KV bytes pa_decode_verify's partition kernel reads for this plan
+ * (every work item's 16-token pages of K and V through the block table, and
+ * for FP8 KV the pages' scales), with the same direct global-to-LDS loads,
+ * one workgroup per work item, and computes and writes nothing. Its kernel
+ * time is the time the plan's bytes and page pattern take on their own, the
+ * floor against which the partition kernel's streaming is judged.
+ * Source: ATOM #2843 ("keep MTP-5 decode on FlyDSL pa_decode past the gluon
+ * query-length limit", Follow-up in aiter: per-kernel microbenchmarks are
+ * how the pages weigh this kernel). Enqueued on `stream`; allocation-free.
+ * Returns PA_E_INVALID for a missing pointer, scales given for bf16 KV or
+ * missing for FP8 KV, or a host-only plan; PA_E_HIP if the launch fails.
+ */
+pa_status pa_stream_floor(const pa_plan_t* plan, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const float* k_scales,
+                          const float* v_scales, void* stream);
+
 /* Release a plan and its device memory. NULL-safe. The caller makes sure no
  * call that uses the plan is still in flight. */
 void pa_free(pa_plan_t* plan);
@@ -302,9 +320,9 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
 /*
  * Optional timing hook: when both are non-NULL (hipEvent_t handles on the
  * plan's device), every later pa_decode_verify launches the partition kernel
- * with the two events attached (hipExtLaunchKernelGGL), so `before` and
- * `after` take that kernel's own start and end timestamps on the call's
- * stream. Pass NULLs to stop (a call to be captured in a graph should run
+ * (and pa_stream_floor its kernel) with the two events attached
+ * (hipExtLaunchKernelGGL), so `before` and `after` take that kernel's own
+ * start and end timestamps on the call's stream. Pass NULLs to stop (a call to be captured in a graph should run
  * without them). Timing is the only effect; results are unchanged.
  */
 pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);

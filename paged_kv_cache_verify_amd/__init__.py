@@ -2,7 +2,7 @@
 
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
 pa_decode_verify_dev, pa_decode_verify_noalloc, pa_kv_append, pa_verify_greedy, pa_free,
-pa_last_error, pa_plan_info, pa_plan_items, pa_set_partition_events). This module only marshals arguments: torch tensors
+pa_last_error, pa_plan_info, pa_plan_items, pa_set_partition_events, pa_stream_floor). This module only marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
 there is no other path, and loading fails loudly if the library is missing.
@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_H
                 4: "PA_E_NOMEM"}
 EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_decode_verify_noalloc",
             "pa_kv_append", "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info",
-            "pa_plan_items", "pa_set_partition_events")
+            "pa_plan_items", "pa_set_partition_events", "pa_stream_floor")
 
 
 class PaShape(ctypes.Structure):
@@ -89,6 +89,8 @@ def library() -> ctypes.CDLL:
         lib.pa_plan_items.restype = ctypes.c_int
         lib.pa_set_partition_events.argtypes = [P, P, P]
         lib.pa_set_partition_events.restype = ctypes.c_int
+        lib.pa_stream_floor.argtypes = [P, P, P, P, P, P, P]
+        lib.pa_stream_floor.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -245,6 +247,14 @@ def pa_verify_greedy(plan: Plan, logits, input_ids, out_ids, accepted, next_ids,
                                       logits.shape[1], logits.stride(0), _ptr(input_ids),
                                       _ptr(out_ids), _ptr(accepted), _ptr(next_ids),
                                       _stream_handle(stream)))
+
+
+def pa_stream_floor(plan: Plan, k_pool, v_pool, block_table, k_scales=None, v_scales=None,
+                    stream=None) -> None:
+    """Measurement: read the plan's KV bytes with the partition kernel's
+    loads and compute nothing (see pa_stream_floor in include/pa_verify.h)."""
+    _check(library().pa_stream_floor(plan.handle, _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                     _ptr(k_scales), _ptr(v_scales), _stream_handle(stream)))
 
 
 def pa_free(plan: Plan) -> None:

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpa_verify.so")
 SOURCES = [os.path.join(CSRC, "pa_plan.cpp"), os.path.join(CSRC, "pa_kernels.hip"),
            os.path.join(CSRC, "pa_append.hip"), os.path.join(CSRC, "pa_verdict.hip"),
-           os.path.join(CSRC, "pa_noalloc.hip")]
+           os.path.join(CSRC, "pa_noalloc.hip"), os.path.join(CSRC, "pa_stream_floor.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

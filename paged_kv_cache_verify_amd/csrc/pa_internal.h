@@ -144,6 +144,11 @@ hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_
 hipError_t launch_reduce_stage1(const KernelArgs& a, int n_chunks, int head_dim, int rows_stride,
                                 hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int head_dim, bool fp8, hipStream_t stream);
+// The streaming-floor measurement kernel over a plan's work items (timing
+// events as for launch_partition).
+hipError_t launch_stream_floor(const KernelArgs& a, int n_items, int head_dim, bool fp8,
+                               hipStream_t stream, hipEvent_t ev_start = nullptr,
+                               hipEvent_t ev_stop = nullptr);
 
 // The zero-allocation attention call's scratch: a file-scope device array of
 // this many bytes (pa_noalloc.hip), one copy per device the library runs on.

@@ -207,8 +207,8 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // compute per SIMD, and the role rotation below only spreads the compute
 // waves over the SIMDs within one workgroup; two one-group workgroups
 // measured 6% slower on a mixed FP8 batch.)
-template <int NG, int TW>
-constexpr int kThreads = 64 * NG * (TW + 1);
+template <int NG, int TW, int NL>
+constexpr int kThreads = 64 * NG * (TW + NL);
 // Ring bytes per group.
 template <int NG, int OCC>
 constexpr int kGroupRingBytes = OCC == 2 ? 72 * 1024 / NG : (NG == 2 ? 76 * 1024 : 38 * 1024);
@@ -221,8 +221,8 @@ struct Ring {
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
-  // Loads per chunk, all issued by the group's loader wave: 1 KiB ones of
-  // K and V, and (FP8) one of the scales.
+  // Loads per chunk: 1 KiB ones of K and V, and (FP8) one of the scales.
+  // Load j of a chunk is issued by the group's issuer j mod P (below).
   static constexpr int T = 2 * C::KLD + C::VLD + (FP8 ? 1 : 0);
   static_assert(STAGE % 256 == 0 && KB % 256 == 0, "stage addresses keep their low 8 bits zero");
 };
@@ -237,11 +237,17 @@ struct RingN : Ring<D, FP8> {
   // early burst measured ~10 us slower over a multi-round call than four.
   static constexpr int R = R0 < 4 ? R0 : 4;
   static_assert(R >= 3, "the ring needs enough stages to keep loads in flight");
-  // Loads the loader may still have in flight when its group starts on a
-  // step: the step's chunk must have landed, the next R - 2 may be pending.
-  static constexpr int WAIT = (R - 2) * S::T;
-  static_assert(WAIT <= 63, "vmcnt holds at most 63");
+  static_assert((R - 2) * S::T <= 63, "vmcnt holds at most 63");
   static constexpr int RING = R * S::STAGE;      // bytes per group
+};
+
+// The loads of one chunk that issuer i of a group's P issuers makes (load j
+// goes to issuer j mod P): T / P, one more for the first T mod P issuers.
+template <int T, int P>
+struct Share {
+  static constexpr int LO = T / P;
+  static constexpr int HI = LO + (T % P ? 1 : 0);
+  static constexpr int NHI = T % P;  // issuers with HI loads
 };
 
 // The ring starts 1 KiB aligned, and stages are multiples of 256 bytes: the
@@ -297,17 +303,18 @@ __device__ __forceinline__ void chunk_pages(uint32_t pages_addr, int k, int& pa,
   pb = __builtin_amdgcn_readfirstlane(pp[1]);
 }
 
-// All loads of one chunk into stage `sb` of the group's ring, issued by the
-// group's loader wave: K of the chunk's two pages (KLD loads of 1 KiB per
-// page, in MFMA operand order: lane l of load u sits at byte 1024 u + 16 l
-// and is what lane l of the MFMA reads back), V of the two pages into the
-// swizzled tile (lane l fetches whichever source chunk belongs at its tile
-// position), and the FP8 scales. The lane's offsets are derived on every
-// call (the empty asm hides that they never change), rather than held in
-// registers across the loop.
-template <int D, bool FP8>
+// Issuer `ii` of P's loads of one chunk into stage `sb` of the group's ring
+// (load j when j mod P == ii): K of the chunk's two pages (KLD loads of
+// 1 KiB per page, in MFMA operand order: lane l of load u sits at byte
+// 1024 u + 16 l and is what lane l of the MFMA reads back), V of the two
+// pages into the swizzled tile (lane l fetches whichever source chunk
+// belongs at its tile position), and the FP8 scales. `ii` is wave-uniform,
+// so the selection is a scalar branch per load. The lane's offsets are
+// derived on every call (the empty asm hides that they never change),
+// rather than held in registers across the loop.
+template <int D, bool FP8, int P>
 __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* sb, int pa,
-                                            int pb, int g, int lane) {
+                                            int pb, int g, int lane, int ii) {
   using C = Cfg<D, FP8>;
   using RG = Ring<D, FP8>;
   int ln = lane;
@@ -321,6 +328,7 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
     unsigned char* dst = sb + half * C::KLD * 1024;
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u) {
+      if ((half * C::KLD + u) % P != ii) continue;
       // bf16: load u covers d = 32 u + 8 (l / 16) .. +8 (contraction step u).
       const uint32_t du = FP8 ? (D >= 128 ? 128 * (u >> 1) + 16 * (u & 1) : 0) : 64 * u;
       dma16(src + (koff + du), dst + u * 1024);
@@ -334,6 +342,7 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
     unsigned char* dst = sb + RG::KB + half * (C::BLKB);
 #pragma unroll
     for (int u = 0; u < C::VLD / 2; ++u) {
+      if ((2 * C::KLD + half * (C::VLD / 2) + u) % P != ii) continue;
       const int pos = u * 1024 + ln * 16;  // byte position in this page's half of the tile
       const int tp = pos / C::ROWB;        // token within the page
       const int t = 16 * half + tp;        // token within the chunk (sets the swizzle)
@@ -342,11 +351,13 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
     }
   }
   if constexpr (FP8) {  // scales: [K page A][K page B][V page A][V page B] x 16 tokens
-    const int which = ln >> 4, tok = ln & 15;
-    const int pgs = (which & 1) ? pb : pa;
-    const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
-                        ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
-    dma4(src2, sb + RG::KB + RG::VB);
+    if ((2 * C::KLD + C::VLD) % P == ii) {
+      const int which = ln >> 4, tok = ln & 15;
+      const int pgs = (which & 1) ? pb : pa;
+      const float* src2 = ((which < 2) ? A.k_scales : A.v_scales) +
+                          ((int64_t)pgs * A.num_kv_heads + g) * kBlock + tok;
+      dma4(src2, sb + RG::KB + RG::VB);
+    }
   }
 }
 
@@ -732,7 +743,13 @@ __device__ __forceinline__ uint32_t vcode_lane_off(int lane) {
   return t * Cfg<D, true>::ROWB + (vswz<D, true>(t) << 4) + 8 * k;
 }
 
-template <int D>
+// ASM_TR: the V code columns are read by one asm block (ending in
+// lgkmcnt(0)) issued with the K reads, ahead of the QK products. Tile waves
+// that also issue ring loads need it: the compiler drains every outstanding
+// direct-to-LDS load (vmcnt(0)) before the transposing-read builtin.
+// Otherwise the builtin lets the compiler spread the reads over the QK
+// products.
+template <int D, bool ASM_TR>
 __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chunk<D>& X,
                                              const unsigned char* st, int tok0, int tv0, int tv1,
                                              int L, int q, int W, float scale_log2, int lane,
@@ -744,10 +761,10 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
   const unsigned char* scl = st + RG::KB + RG::VB;
   X.tok0 = tok0;
 
-  // ---- S^T = K Q^T, the K operands read page by page.
+  // ---- S^T = K Q^T: the K operands of both pages, then the products.
+  i32x8 kop[2][C::KS8];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS8; ++ks) {
       u32x4 x0, x1;
@@ -762,10 +779,28 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
         x1 = *reinterpret_cast<const u32x4*>(st + bb * 1024 + (i16 + 16 * (cc + 1)) * 16);
         if (c >= 2) x0 = x1 = u32x4{0, 0, 0, 0};
       }
-      const i32x8 kop = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      acc = mfma_fp8(kop, S.Q.hi[ks], acc);
-      acc = mfma_fp8(kop, S.Q.lo[ks], acc);
+      kop[bb][ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  }
+  if constexpr (ASM_TR) {
+    // The V code columns, in one asm block whose lgkmcnt(0) also covers the
+    // K reads above (voff: vcode_lane_off; see below for the addresses).
+    uint32_t vo = voff;
+    asm volatile("" : "+v"(vo));  // keep the per-tile addresses out of the loop
+    const uint32_t vbase = lds_addr(st + RG::KB) + vo;
+    uint32_t va[C::MT];
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) va[mt] = vbase ^ (uint32_t)(mt << 4);
+    vt_reads_b8<C::MT>(X.vcode, va);
+  }
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS8; ++ks) {
+      acc = mfma_fp8(kop[bb][ks], S.Q.hi[ks], acc);
+      acc = mfma_fp8(kop[bb][ks], S.Q.lo[ks], acc);
     }
     X.sc[bb] = acc;
   }
@@ -782,7 +817,7 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
   // address is a fixed XOR of one base. (The compute waves issue no
   // direct-to-LDS loads, so the compiler's own waits around these reads
   // cost nothing.)
-  {
+  if constexpr (!ASM_TR) {
     uint32_t vo = voff;
     asm volatile("" : "+v"(vo));  // keep the per-tile addresses out of the loop
     const uint32_t vbase = lds_addr(st + RG::KB) + vo;
@@ -947,11 +982,24 @@ __device__ __forceinline__ void load_query_fp8(QOps<D, true>& Q, const uint16_t*
   }
 }
 
-template <int D, bool FP8, int NG, int TW, int OCC>
-__global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(KernelArgs A) {
+// Rotation of the roles in the second of two token groups: it puts that
+// group's tile 0 on SIMD 2 (wave w runs on SIMD w mod 4), so that the two
+// groups' first tiles use different SIMDs.
+constexpr int rot2(int GW) {
+  const int slot0 = (((2 - GW) % 4) + 4) % 4;  // group 1's slot on SIMD 2
+  return (GW - slot0) % GW;
+}
+
+// NL: loader waves per token group. CL: whether the tile waves also issue a
+// share of their group's ring loads (then P = NL + TW issuers per group,
+// else P = NL).
+template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL>
+__global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
   using RG = RingN<D, FP8, NG, OCC>;
-  constexpr int GW = TW + 1;  // waves per group
+  constexpr int GW = TW + NL;            // waves per group
+  constexpr int P = NL + (CL ? TW : 0);  // load issuers per group
+  using SH = Share<RG::T, P>;
   using SM = Smem<D, FP8, NG, TW, OCC>;
   static_assert(OCC == 1 || sizeof(SM) <= 80 * 1024, "two workgroups share a CU's LDS");
   __shared__ SM sm;
@@ -959,16 +1007,21 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // Token group gp, role r (row tile r < TW, or the loader). The roles
+  // Token group gp, role r (row tile r < TW, or loader r - TW). The roles
   // rotate by group so that the tile waves spread over the SIMDs (wave w
-  // runs on SIMD w mod 4): with four groups of three tile waves every SIMD
-  // hosts three of them and one loader; with two groups the second group's
-  // tiles 0 and 1 sit on the two SIMDs the first group's tiles 0 and 1 do
-  // not use, so items of up to two tiles run one compute wave per SIMD.
-  constexpr int kRot = NG == 4 ? 1 : (GW == 5 ? 4 : 2);
+  // runs on SIMD w mod 4): with four groups of three tile waves and a loader
+  // every SIMD hosts three tile waves and one loader; with two groups the
+  // second group's tiles 0 and 1 sit on the two SIMDs the first group's
+  // tiles 0 and 1 do not use, so items of up to two tiles run one compute
+  // wave per SIMD.
+  constexpr int kRot = NG == 4 ? 1 : (NG == 2 ? rot2(GW) : 0);
   const int gp = w / GW, slot = w % GW;
   const int r = (slot + gp * kRot) % GW;
-  const bool loader = r == TW;
+  const bool loader = r >= TW;
+  // Ring-load issuer index within the group: loaders first, then (CL) the
+  // tile waves.
+  const int ii = loader ? r - TW : NL + r;
+  const bool issuer = loader || CL;
   const int n = lane & 15, c = lane >> 4;
   const int b = it.seq, g = it.kv_head;
   const int G = A.group, Hq = A.num_q_heads;
@@ -999,12 +1052,13 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   // Page ids of every chunk (a page past the item's end repeats the
   // chunk's first page, whose slots the masks then exclude).
   const int32_t* bt = A.block_table + (int64_t)b * A.max_blocks;
-  // The loader starts its group's first R - 1 chunks at once while the
-  // other waves fill the page table and load the query. One vector load
-  // brings every page id those chunks need: lane j < 2 (R - 1) reads chunk
-  // j / 2's page j % 2 (the chunk's first page where its second lies past
-  // the item). (Scalar loads of the same entries came back up to 2.5 us
-  // later than vector loads, and held the later groups' loaders back.)
+  // The loaders start their group's first R - 1 chunks at once (loader i of
+  // NL issues load j of each when j mod NL == i) while the other waves fill
+  // the page table and load the query. One vector load brings every page id
+  // those chunks need: lane j < 2 (R - 1) reads chunk j / 2's page j % 2
+  // (the chunk's first page where its second lies past the item). (Scalar
+  // loads of the same entries came back up to 2.5 us later than vector
+  // loads, and held the later groups' loaders back.)
   if (loader) {
     int pid = 0;
     {
@@ -1028,7 +1082,7 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
 #pragma unroll
     for (int k = 0; k < RG::R - 1; ++k)
       if (gp + NG * k < nch)
-        issue_chunk<D, FP8>(A, sm.ring[gp] + k * RG::STAGE, pa[k], pb[k], g, lane);
+        issue_chunk<D, FP8, NL>(A, sm.ring[gp] + k * RG::STAGE, pa[k], pb[k], g, lane, r - TW);
   }
   constexpr int kFillThreads = NG * TW * 64;
   const int fill_tid = (gp * TW + (loader ? 0 : r)) * 64 + lane;
@@ -1074,24 +1128,34 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
 
-  // Chunk of this wave's group at step k: gp + 2 k. The loader filled the
-  // first R - 1 stages above; then per step: the loader waits for its loads
-  // of the step's chunk, the barrier (every group's chunk has landed and
-  // every wave is done with the stage about to be refilled), the loader
-  // refills that stage while the compute waves work. Compute waves never
-  // issue or wait for ring loads, so they never stall behind the load queue.
-  // One step: the loader's wait, the barrier, the loader's refill.
+  // Chunk of this wave's group at step k: gp + NG k. The loaders filled the
+  // first R - 1 stages above; then per step: every issuer waits for its
+  // loads of the step's chunk, the barrier (every group's chunk has landed
+  // and every wave is done with the stage about to be refilled), the
+  // issuers refill that stage (issuer ii of P making load j when j mod P ==
+  // ii) while the tile waves work.
+  //
+  // The waits are per issuer: after the step's chunk, an issuer has made at
+  // most its share of each of the next R - 2 chunks (the loaders' share of a
+  // prologue chunk is larger, so the wait is then stricter than needed,
+  // never looser); waiting until no more than R - 2 shares are pending
+  // therefore covers its part of the step's chunk.
   auto step_begin = [&](int k) __attribute__((always_inline)) {
-    if (loader) {  // this step's chunk has landed; the next R - 2 may be pending
-      if (gp + NG * (k + RG::R - 2) < nch) wait_vm<RG::WAIT>();
-      else wait_vm<0>();
+    if (issuer) {
+      if (gp + NG * (k + RG::R - 2) < nch) {
+        if (ii < SH::NHI) wait_vm<(RG::R - 2) * SH::HI>();
+        else wait_vm<(RG::R - 2) * SH::LO>();
+      } else {
+        wait_vm<0>();
+      }
     }
     ring_barrier();
     const int cn = gp + NG * (k + RG::R - 1);
-    if (loader && cn < nch) {
+    if (issuer && cn < nch) {
       int pa, pb;
       chunk_pages(pages_addr, cn, pa, pb);
-      issue_chunk<D, FP8>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, lane);
+      issue_chunk<D, FP8, P>(A, ring + ((k + RG::R - 1) % RG::R) * RG::STAGE, pa, pb, g, lane,
+                             ii);
     }
   };
   if constexpr (!FP8) {
@@ -1118,8 +1182,8 @@ __global__ __launch_bounds__((kThreads<NG, TW>), 1) void pa_partition_kernel(Ker
         const int ck = gp + NG * k;
         step_begin(k);
         if (active && ck < nch) {
-          if (chunk_scores<D>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk, tv0,
-                              tv1, L, q, W, sl, lane, voff)) {
+          if (chunk_scores<D, CL>(S, X, ring + (k % RG::R) * RG::STAGE, tokbase + ck * kChunk,
+                                  tv0, tv1, L, q, W, sl, lane, voff)) {
             moved = true;
             break;
           }
@@ -1357,15 +1421,15 @@ __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A
 // timing events the launch carries them itself (hipExtLaunchKernelGGL), so
 // they take the kernel's own start and end timestamps, as a kernel trace
 // does, rather than those of marker packets around its dispatch.
-template <int D, bool FP8, int NG, int TW, int OCC>
+template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL>
 static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream, hipEvent_t ev_start,
                        hipEvent_t ev_stop) {
   if (ev_start && ev_stop)
-    hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
-                          dim3(kThreads<NG, TW>), 0, stream, ev_start, ev_stop, 0, a);
+    hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL>), dim3(n_items),
+                          dim3(kThreads<NG, TW, NL>), 0, stream, ev_start, ev_stop, 0, a);
   else
-    hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, OCC>), dim3(n_items),
-                       dim3(kThreads<NG, TW>), 0, stream, a);
+    hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL>), dim3(n_items),
+                       dim3(kThreads<NG, TW, NL>), 0, stream, a);
 }
 
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
@@ -1375,20 +1439,20 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
   if (ntmax < 1 || (occ != 1 && occ != 2)) return hipErrorInvalidValue;
   if (head_dim == 256) {  // FP8 KV only, at most 48 rows; one workgroup per CU
     if (!fp8 || ntmax > 3) return hipErrorInvalidValue;
-    launch_one<256, true, 2, 3, 1>(a, n_items, stream, ev_start, ev_stop);
+    launch_one<256, true, 2, 3, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
     return hipGetLastError();
   }
   if (ntmax > 4) return hipErrorInvalidValue;
   if (fp8 && occ != 1) return hipErrorInvalidValue;  // FP8 runs one workgroup per CU
   if (head_dim == 128) {
-    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1>(a, n_items, stream, ev_start, ev_stop);
-    else if (fp8) launch_one<128, true, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
-    else if (occ == 1) launch_one<128, false, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
-    else launch_one<128, false, 1, 4, 2>(a, n_items, stream, ev_start, ev_stop);
+    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    else if (fp8) launch_one<128, true, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, ev_start, ev_stop);
   } else {
-    if (fp8) launch_one<64, true, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
-    else if (occ == 1) launch_one<64, false, 2, 4, 1>(a, n_items, stream, ev_start, ev_stop);
-    else launch_one<64, false, 1, 4, 2>(a, n_items, stream, ev_start, ev_stop);
+    if (fp8) launch_one<64, true, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    else if (occ == 1) launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    else launch_one<64, false, 1, 4, 1, 2, false>(a, n_items, stream, ev_start, ev_stop);
   }
   return hipGetLastError();
 }

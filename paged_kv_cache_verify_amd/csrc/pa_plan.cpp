@@ -720,6 +720,34 @@ pa_status pa_decode_verify_noalloc(const pa_plan_t* plan, const void* q, const v
                      out, hs);
 }
 
+pa_status pa_stream_floor(const pa_plan_t* plan, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const float* k_scales,
+                          const float* v_scales, void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
+  const pa_shape& s = plan->shape;
+  const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
+  if (plan->items.empty()) return PA_OK;
+  if (!k_pool || !v_pool || !block_table)
+    return fail(PA_E_INVALID, "k_pool, v_pool and block_table are required");
+  if (fp8 != (k_scales && v_scales))
+    return fail(PA_E_INVALID, "scales are required exactly for FP8 KV");
+  KernelArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.items = plan->d_items;
+  a.num_kv_heads = s.num_kv_heads;
+  a.max_blocks = s.max_blocks_per_seq;
+  const hipError_t e = launch_stream_floor(a, (int)plan->items.size(), s.head_dim, fp8,
+                                           static_cast<hipStream_t>(stream), plan->ev_before,
+                                           plan->ev_after);
+  if (e != hipSuccess) return hip_fail(e, "stream floor kernel launch");
+  return PA_OK;
+}
+
 pa_status pa_kv_append(const pa_plan_t* plan, const void* k_new, const void* v_new,
                        const int32_t* block_table, void* k_pool, void* v_pool,
                        float* k_scales, float* v_scales, void* stream) {

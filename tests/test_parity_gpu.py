@@ -436,3 +436,23 @@ def test_graph_capture_two_level_and_row_block_reduce():
     kw.pop("windowed")
     ctx, q = _many_pairs(B, 11 + B, qs)
     _graph_replays_match_eager(edge("graph many pairs", ctx_lens=ctx, q_lens=q, **kw), 32)
+
+
+@pytest.mark.parametrize("cfg,kw", [(2, dict(scale_ctx=1 / 16)), (3, dict(scale_ctx=1 / 8, num_seqs=12)),
+                                    (6, dict(scale_ctx=1 / 32, num_seqs=4))])
+def test_stream_floor_reads_and_writes_nothing(cfg, kw):
+    """The measurement call pa_stream_floor streams a plan's pages and
+    computes nothing: it runs at every (head dim, KV dtype) the bench uses
+    and leaves the pools (and everything else it is given) untouched."""
+    wl = workloads.make(cfg, **kw)
+    dev = wl.to("cuda:0")
+    before = [None if t is None else t.clone() for t in (dev.k_pool, dev.v_pool, dev.k_scales,
+                                                         dev.v_scales, dev.block_table)]
+    plan = pav.plan_for(dev, device=0)
+    pav.pa_stream_floor(plan, dev.k_pool, dev.v_pool, dev.block_table, dev.k_scales, dev.v_scales)
+    torch.cuda.synchronize()
+    pav.pa_free(plan)
+    for b, a in zip(before, (dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales,
+                             dev.block_table)):
+        if b is not None:
+            assert torch.equal(b.view(torch.uint8), a.view(torch.uint8))
