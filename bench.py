@@ -291,6 +291,70 @@ def measure_verdict(q_lens, vocab: int, steps: int, warmup: int):
             "timed_as": "hip-graph replay (logits resident in the Infinity Cache)"}
 
 
+def spacing_study(cfg: int, partition_tokens, steps: int):
+    """Run the same calls of workload `cfg` four ways, each `steps` calls
+    after a synchronisation: eager launches, one replayed HIP graph, and both
+    again with a ~20 us spin (torch.cuda._sleep) after every call. Under
+    `rocprofv3 --kernel-trace` the partition kernel's durations per phase
+    show whether calls run back to back are slower than spaced ones. Prints
+    the host time per phase; the kernel durations come from the trace."""
+    import torch
+
+    import paged_kv_cache_verify_amd as pav
+    import workloads
+
+    wl = workloads.make(cfg)
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0, partition_tokens=partition_tokens)
+    kv = plan.info()["kv_bytes"]
+    copies = 1 if kv >= (1 << 30) else int(math.ceil((1 << 30) / kv)) + 1
+    pools = [(dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales)]
+    for _ in range(copies - 1):
+        pools.append(tuple(None if t is None else t.clone() for t in pools[0]))
+    dt = torch.float32 if wl.out_dtype == "fp32" else torch.bfloat16
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda:0")
+    s = torch.cuda.Stream()
+
+    def call(i, spin):
+        kp, vp, ks, vs = pools[i % copies]
+        pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out, s)
+        if spin:
+            torch.cuda._sleep(50000)
+
+    with torch.cuda.stream(s):
+        for i in range(3):
+            call(i, False)
+    torch.cuda.synchronize()
+    graphs = {}
+    for spin in (False, True):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                call(i, spin)
+        graphs[spin] = g
+    torch.cuda.synchronize()
+    res = {}
+    for spin in (False, True):
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            for i in range(steps):
+                call(i, spin)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        with torch.cuda.stream(s):
+            graphs[spin].replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        tag = " + spin" if spin else ""
+        res["eager" + tag] = round(1e6 * (t1 - t0) / steps, 2)
+        res["graph" + tag] = round(1e6 * (t2 - t1) / steps, 2)
+    pav.pa_free(plan)
+    print(json.dumps({"spacing_study": wl.name, "steps": steps,
+                      "phases_in_order": ["warm-up x3", "eager", "graph", "eager + spin",
+                                          "graph + spin"],
+                      "host_us_per_call": res}), flush=True)
+
+
 def cpu_baseline(wl, budget_s: float = 10.0):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -330,6 +394,8 @@ def main():
                     help="time just this workload (2..6) and print its figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--spacing", type=int, default=None,
+                    help="run the back-to-back vs spaced study on this workload and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -346,6 +412,9 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.spacing is not None:
+        spacing_study(args.spacing, args.partition_tokens, min(args.steps, 40))
+        return
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
