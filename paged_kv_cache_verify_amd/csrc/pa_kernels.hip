@@ -68,13 +68,7 @@ __device__ __forceinline__ int qk_dmap(int s, int c) { return 32 * s + 8 * c; }
 // FP8 QK runs on v_mfma_f32_16x16x128_f8f6f4 with the codes as they are:
 // lane l holds 32 codes of token (or query row) l % 16 at d = 128 ks +
 // 32 (l / 16) + j, j = 0..31, for both operands (at D 64 lane groups 2 and 3
-// hold zeros). In the ring, K load u of a page puts the 16 bytes of token
-// l % 16 at d = 128 (u / 2) + 32 (l / 16) + 16 (u % 2) at byte 1024 u + 16 l
-// (D 64: one load, d = 16 (l / 16)).
-template <int D>
-__device__ __forceinline__ int k8_src(int u, int c) {
-  return D >= 128 ? 128 * (u >> 1) + 32 * c + 16 * (u & 1) : 16 * c;
-}
+// hold zeros).
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
@@ -180,6 +174,27 @@ __device__ __forceinline__ int vtile_chunk(int t, int chunk) {
   return t * ROWB + ((chunk ^ vswz<D, FP8>(t)) << 4);
 }
 
+// LDS K tile of one page: its 16 token rows of ROWB bytes, token-major as in
+// the pool, with the 16-byte chunks of row t XOR-swizzled by kswz(t). The
+// direct-to-LDS loads then fetch whole token rows (every 1 KiB load covers
+// full cache lines: a load of 16 rows x 64 bytes, the MFMA operand order,
+// streamed at about 80% of the rate of whole rows), and the operand reads,
+// in which 16 lanes read one chunk index of 16 consecutive rows, hit
+// distinct banks: the swizzle spreads those rows over all sixteen 16-byte
+// slots of a 256-byte bank window.
+template <int D, bool FP8>
+__device__ __forceinline__ int kswz(int t) {
+  constexpr int ROWB = D * (FP8 ? 1 : 2);
+  constexpr int RPW = 256 / ROWB;  // token rows per 256-byte bank window
+  constexpr int CPR = ROWB / 16;   // 16-byte chunks per row
+  return (t / RPW) % CPR;
+}
+template <int D, bool FP8>
+__device__ __forceinline__ int ktile_chunk(int t, int chunk) {
+  constexpr int ROWB = D * (FP8 ? 1 : 2);
+  return t * ROWB + ((chunk ^ kswz<D, FP8>(t)) << 4);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
@@ -217,7 +232,7 @@ constexpr int kGroupRingBytes = OCC == 2 ? 72 * 1024 / NG : (NG == 2 ? 76 * 1024
 template <int D, bool FP8>
 struct Ring {
   using C = Cfg<D, FP8>;
-  static constexpr int KB = 2 * C::KLD * 1024;   // K of two pages, operand order
+  static constexpr int KB = 2 * C::KLD * 1024;   // K tiles of two pages (swizzled rows)
   static constexpr int VB = C::VLD * 1024;       // V tile of two pages
   static constexpr int SB = FP8 ? 256 : 0;       // K and V scales of two pages
   static constexpr int STAGE = KB + VB + SB;
@@ -305,10 +320,10 @@ __device__ __forceinline__ void chunk_pages(uint32_t pages_addr, int k, int& pa,
 
 // Issuer `ii` of P's loads of one chunk into stage `sb` of the group's ring
 // (load j when j mod P == ii): K of the chunk's two pages (KLD loads of
-// 1 KiB per page, in MFMA operand order: lane l of load u sits at byte
-// 1024 u + 16 l and is what lane l of the MFMA reads back), V of the two
-// pages into the swizzled tile (lane l fetches whichever source chunk
-// belongs at its tile position), and the FP8 scales. `ii` is wave-uniform,
+// 1 KiB per page) into their swizzled K tiles and V of the two pages into
+// the swizzled V tile (in both, lane l fetches whichever source chunk
+// belongs at its tile position, so every load reads whole token rows), and
+// the FP8 scales. `ii` is wave-uniform,
 // so the selection is a scalar branch per load. The lane's offsets are
 // derived on every call (the empty asm hides that they never change),
 // rather than held in registers across the loop.
@@ -319,19 +334,19 @@ __device__ __forceinline__ void issue_chunk(const KernelArgs& A, unsigned char* 
   using RG = Ring<D, FP8>;
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const uint32_t koff = (ln & 15) * C::ROWB + (FP8 ? k8_src<D>(0, ln >> 4) : 16 * (ln >> 4));
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int page = half ? pb : pa;
     const char* src = static_cast<const char*>(A.k_pool) +
                       ((int64_t)page * A.num_kv_heads + g) * C::BLKB;
-    unsigned char* dst = sb + half * C::KLD * 1024;
+    unsigned char* dst = sb + half * C::BLKB;
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u) {
       if ((half * C::KLD + u) % P != ii) continue;
-      // bf16: load u covers d = 32 u + 8 (l / 16) .. +8 (contraction step u).
-      const uint32_t du = FP8 ? (D >= 128 ? 128 * (u >> 1) + 16 * (u & 1) : 0) : 64 * u;
-      dma16(src + (koff + du), dst + u * 1024);
+      const int pos = u * 1024 + ln * 16;  // byte position in this page's K tile
+      const int tp = pos / C::ROWB;        // its token row
+      const int ch = ((pos % C::ROWB) >> 4) ^ kswz<D, FP8>(tp);  // its source chunk
+      dma16(src + (uint32_t)(tp * C::ROWB + ch * 16), dst + u * 1024);
     }
   }
 #pragma unroll
@@ -580,12 +595,14 @@ __device__ __forceinline__ void compute_chunk(WaveState<D, false>& S, const unsi
   // ---- LDS reads of the chunk: K operands, then every V^T operand (one
   // asm block whose lgkmcnt(0) also covers the K reads), so both latencies
   // overlap.
+  // Contraction step u of token row i16 is chunk 4 u + c of its K tile row.
   u32x4 kr[2][C::KLD];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
     for (int u = 0; u < C::KLD; ++u)
-      kr[bb][u] = *reinterpret_cast<const u32x4*>(kv + (bb * C::KLD + u) * 1024 + lane * 16);
+      kr[bb][u] = *reinterpret_cast<const u32x4*>(kv + bb * C::BLKB +
+                                                  ktile_chunk<D, false>(i16, 4 * u + c));
   const uint32_t vt = lds_addr(kv + RG::KB);
   uint32_t va[C::MT];
 #pragma unroll
@@ -767,16 +784,14 @@ __device__ __forceinline__ bool chunk_scores(const WaveState<D, true>& S, Fp8Chu
   for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
     for (int ks = 0; ks < C::KS8; ++ks) {
-      u32x4 x0, x1;
-      if constexpr (D >= 128) {
-        x0 = *reinterpret_cast<const u32x4*>(st + (bb * C::KLD + 2 * ks) * 1024 + lane * 16);
-        x1 = *reinterpret_cast<const u32x4*>(st + (bb * C::KLD + 2 * ks + 1) * 1024 + lane * 16);
-      } else {
-        // D 64: d = 32 c + 0..15 and + 16..31 sit with lane groups 2c and
-        // 2c + 1 of the page's one load; groups 2 and 3 carry zeros.
-        const int cc = (2 * c) & 3;
-        x0 = *reinterpret_cast<const u32x4*>(st + bb * 1024 + (i16 + 16 * cc) * 16);
-        x1 = *reinterpret_cast<const u32x4*>(st + bb * 1024 + (i16 + 16 * (cc + 1)) * 16);
+      // Token row i16's codes d = 128 ks + 32 c .. +32: chunks 8 ks + 2 c
+      // and the next one of its K tile row (D 64: lane groups 2 and 3 carry
+      // zeros).
+      const int ch = 8 * ks + 2 * (D >= 128 ? c : (c & 1));
+      const unsigned char* kt = st + bb * C::BLKB;
+      u32x4 x0 = *reinterpret_cast<const u32x4*>(kt + ktile_chunk<D, true>(i16, ch));
+      u32x4 x1 = *reinterpret_cast<const u32x4*>(kt + ktile_chunk<D, true>(i16, ch + 1));
+      if constexpr (D < 128) {
         if (c >= 2) x0 = x1 = u32x4{0, 0, 0, 0};
       }
       kop[bb][ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
