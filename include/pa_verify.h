@@ -177,6 +177,40 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
                                void* stream);
 
 /*
+ * The verify-attention call as a single launch: the partition kernel merges
+ * the partial results of every split (sequence, KV head) itself, and no
+ * reduce kernel follows. Source: ATOM #3091 ("High-interactivity monokernel
+ * decode for DeepSeek-V4.1-Flash on MI355X", Summary: a decode layer runs as
+ * one persistent kernel; How to reproduce: full graph capture); ATOM #2843
+ * ("keep MTP-5 decode on FlyDSL pa_decode past the gluon query-length
+ * limit", Change: persistent and non-persistent decode calls are routed
+ * apart).
+ *   context_lens_dev  device [B] int32 lengths read at run time, with the
+ *                     plan's lengths as upper bounds (as pa_decode_verify_dev),
+ *                     or NULL for the plan's own lengths
+ * The work items of a split pair write their partials and then count their
+ * arrival on a device counter of the pair's merge node (a node merges at
+ * most 16 partials; pairs with more go through a tree of nodes, one level
+ * per factor of 16). The workgroup whose arrival completes a node's count
+ * merges that node's partials: into the output at the root, else into an
+ * input of the parent node, where it arrives in turn. The counters are
+ * part of the plan's device memory, zero when pa_plan returns and reset by
+ * each node's last arriver, so every call leaves them at zero (graph replays
+ * included). Calls with one plan that overlap on the device (different
+ * streams or threads) race on the counters and partials and must be
+ * serialised by the caller. Results are pa_decode_verify's up to the order
+ * of the log-sum-exp merge (float rounding). Otherwise as pa_decode_verify:
+ * asynchronous, allocation-free, graph-capturable, the same errors (and
+ * PA_E_INVALID for a windowed plan read with device lengths unless it was
+ * built with lengths_are_bounds = 1).
+ */
+pa_status pa_decode_verify_fused(const pa_plan_t* plan, const int32_t* context_lens_dev,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const float* k_scales,
+                                 const float* v_scales, const float* sinks, void* out,
+                                 void* stream);
+
+/*
  * pa_decode_verify for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the call allocates nothing, and the plan may be a host-only
@@ -297,7 +331,9 @@ const char* pa_last_error(void);
  *                   sequence, Hkv x (visible keys) x (K + V bytes per token,
  *                   plus 8 bytes of FP8 scales)
  *   scratch_bytes   device bytes of the partial results the plan owns
- *                   (with the two-level merge, its first-level partials too)
+ *                   (with the two-level merge, its first-level partials too,
+ *                   and the inner merge nodes' results of the single-launch
+ *                   call)
  *   work_items      number of partition work items (workgroups launched)
  *   partition_tokens keys per work item actually used
  */

@@ -1,8 +1,10 @@
 """Paged verify attention for MI355X: a thin binding over libpa_verify.so.
 
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
-pa_decode_verify_dev, pa_decode_verify_noalloc, pa_kv_append, pa_verify_greedy, pa_free,
-pa_last_error, pa_plan_info, pa_plan_items, pa_set_partition_events, pa_stream_floor). This module only marshals arguments: torch tensors
+pa_decode_verify_dev, pa_decode_verify_fused, pa_decode_verify_noalloc,
+pa_kv_append, pa_verify_greedy, pa_free, pa_last_error, pa_plan_info,
+pa_plan_items, pa_set_partition_events, pa_stream_floor). This module only
+marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
 there is no other path, and loading fails loudly if the library is missing.
@@ -22,8 +24,8 @@ PA_BF16, PA_FP8_E4M3, PA_FP32 = 0, 1, 2
 ITEM_FIELDS = 7  # int32 per work item from pa_plan_items
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
-EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_decode_verify_noalloc",
-            "pa_kv_append", "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info",
+EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_decode_verify_fused",
+            "pa_decode_verify_noalloc", "pa_kv_append", "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info",
             "pa_plan_items", "pa_set_partition_events", "pa_stream_floor")
 
 
@@ -71,6 +73,8 @@ def library() -> ctypes.CDLL:
         lib.pa_decode_verify.restype = ctypes.c_int
         lib.pa_decode_verify_dev.argtypes = [P, P, P, P, P, P, P, P, P, P, P]
         lib.pa_decode_verify_dev.restype = ctypes.c_int
+        lib.pa_decode_verify_fused.argtypes = [P, P, P, P, P, P, P, P, P, P, P]
+        lib.pa_decode_verify_fused.restype = ctypes.c_int
         lib.pa_decode_verify_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P]
         lib.pa_decode_verify_noalloc.restype = ctypes.c_int
         lib.pa_kv_append.argtypes = [P, P, P, P, P, P, P, P, P]
@@ -206,6 +210,17 @@ def pa_decode_verify_dev(plan: Plan, context_lens_dev, q, k_pool, v_pool, block_
                                           _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                           _ptr(k_scales), _ptr(v_scales), _ptr(sinks), _ptr(out),
                                           _stream_handle(stream)))
+
+
+def pa_decode_verify_fused(plan: Plan, context_lens_dev, q, k_pool, v_pool, block_table,
+                           k_scales, v_scales, sinks, out, stream=None) -> None:
+    """The call as a single launch whose split items merge their partials
+    themselves; context_lens_dev is a device int32 [B] tensor of lengths
+    (the plan's are then upper bounds) or None for the plan's own."""
+    _check(library().pa_decode_verify_fused(plan.handle, _ptr(context_lens_dev), _ptr(q),
+                                            _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                            _ptr(k_scales), _ptr(v_scales), _ptr(sinks),
+                                            _ptr(out), _stream_handle(stream)))
 
 
 def pa_decode_verify_noalloc(plan: Plan, q, k_pool, v_pool, block_table, k_scales, v_scales,

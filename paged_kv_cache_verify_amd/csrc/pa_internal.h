@@ -42,6 +42,34 @@ struct WorkItem {
   // the item's packed rows: [row0, row0 + nrows) of the q x G rows
   int32_t row0;
   int32_t nrows;
+  // fused call: the merge node this item's partial arrives at (-1 when
+  // slot < 0)
+  int32_t node;
+  int32_t pad[4];
+};
+
+// Fan-in of a merge node in the fused call: a split pair with at most this
+// many partials is merged in one node, more go through a tree of nodes.
+constexpr int kFusedFanIn = 16;
+
+// One merge of the fused call (single launch, no reduce kernel): n_parts
+// partials, slots [slot_base, slot_base + n_parts) of the partition
+// partials (from_tree 0) or of the tree slots (1), rows [row0, row0 + nrows)
+// of (seq, kv_head). The workgroup whose arrival brings the node's counter
+// to n_parts merges them: into the output (parent < 0), or into tree slot
+// out_slot, after which it arrives at node `parent`.
+struct MergeNode {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t q_len;
+  int32_t q_off;
+  int32_t row0;
+  int32_t nrows;
+  int32_t slot_base;
+  int32_t n_parts;
+  int32_t from_tree;
+  int32_t out_slot;
+  int32_t parent;
   int32_t pad[5];
 };
 
@@ -88,6 +116,13 @@ struct KernelArgs {
   // partials): [chunks][rows_stride][D] and [chunks][rows_stride][2].
   float* l1_o;
   float* l1_ml;
+  // Fused call (null otherwise): merge nodes, one arrival counter per node
+  // (zero between calls: the last arriver resets it), and the tree slots
+  // [slots][rows_stride][D] and [slots][rows_stride][2].
+  const MergeNode* nodes;
+  int32_t* counters;
+  float* tree_o;
+  float* tree_ml;
 };
 
 // The new tokens of a verify step, for the paged KV append kernel.
@@ -132,9 +167,11 @@ hipError_t launch_verdict(const VerdictArgs& a, hipStream_t stream);
 // share a CU, 1 (items fit one round) or 2 (more items than CUs, bf16 KV
 // only).
 // ev_start, ev_stop: optional timing events taken by the launch itself.
+// fused: the single-launch variant, whose split items merge their pair's
+// partials themselves (a.nodes, a.counters, a.tree_o, a.tree_ml set).
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             int occ, hipStream_t stream, hipEvent_t ev_start = nullptr,
-                            hipEvent_t ev_stop = nullptr);
+                            hipEvent_t ev_stop = nullptr, bool fused = false);
 // rows_stride: the most rows any reduce item has; max_parts: the most
 // partials any reduce item merges (picks the reduce kernel's shape).
 hipError_t launch_reduce(const KernelArgs& a, int n_red, int head_dim, int rows_stride,

@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -930,6 +931,121 @@ __device__ __forceinline__ float sink_log2(const KernelArgs& A, int b, int h) {
   return -INFINITY;
 }
 
+// ---- The fused call: split items merge their pair's partials themselves.
+//
+// Partials and tree slots are written and read with device-scope buffer
+// accesses (sc1: the mapping of relaxed device-scope atomic stores and
+// loads on gfx950): the stores write through the XCD's L2, and the loads are
+// not served from another XCD's stale lines. A workgroup waits until its
+// stores have completed before its one atomic arrival at the node, so the
+// workgroup whose arrival completes the node's count finds every partial
+// at the point of coherence. No L2 write-back or invalidation is needed (a
+// device-scope fence per workgroup writes back the XCD's whole L2 and cost
+// more than the separate reduce kernel).
+constexpr int kScopeDevice = 16;  // buffer access cache bits: sc1
+
+// A raw buffer over [base, base + bytes): offsets are 32-bit and accesses
+// past the end read zeros and write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kScopeDevice);
+}
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kScopeDevice);
+}
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kScopeDevice));
+}
+__device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kScopeDevice));
+}
+
+// Arrival of a workgroup whose partial (or tree slot) is written, at merge
+// node `node`; every thread of the workgroup calls it (NT threads). The last
+// arriver resets the node's counter and folds the node's partials, row by
+// row in index order, into the output or into its tree slot, and then
+// arrives at the parent node. s_flag: one int of LDS no wave still uses.
+template <int D, int NT>
+__device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
+  constexpr int COLS = D / 4;
+  constexpr int U = 8;  // partials in flight per thread
+  const int tid = threadIdx.x;
+  for (;;) {
+    wait_vm<0>();  // this wave's stores are complete at device scope
+    __syncthreads();
+    if (tid == 0) {
+      const int need = A.nodes[node].n_parts;
+      const int old =
+          __hip_atomic_fetch_add(A.counters + node, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == need - 1;
+      // Every arrival of this call is counted: zero for the next call.
+      if (last)
+        __hip_atomic_store(A.counters + node, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_flag = last;
+    }
+    __syncthreads();
+    if (!*s_flag) return;  // uniform over the workgroup
+    const MergeNode nd = A.nodes[node];
+    const int64_t RS = A.rows_stride;
+    const float* so = nd.from_tree ? A.tree_o : A.part_o;
+    const float* sm = nd.from_tree ? A.tree_ml : A.part_ml;
+    const uint32_t ostride = (uint32_t)(RS * D * 4), mstride = (uint32_t)(RS * 8);
+    const __amdgpu_buffer_rsrc_t ro = dev_rsrc(so + nd.slot_base * RS * D, ostride * nd.n_parts);
+    const __amdgpu_buffer_rsrc_t rm = dev_rsrc(sm + nd.slot_base * RS * 2, mstride * nd.n_parts);
+    const int n = nd.n_parts;
+    for (int t = tid; t < nd.nrows * COLS; t += NT) {
+      const int row = nd.row0 + t / COLS;  // packed row of the sequence
+      const int d = (t % COLS) * 4;
+      const uint32_t oo = (uint32_t)(row * D + d) * 4, om = (uint32_t)row * 8;
+      float M = -INFINITY, z = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < n; k0 += U) {
+        float2 v[U];
+        f32x4 o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          v[u] = make_float2(-INFINITY, 0.f);
+          o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (k0 + u < n) {
+            v[u] = ld_dev2(rm, om + (k0 + u) * mstride);
+            o[u] = ld_dev4(ro, oo + (k0 + u) * ostride);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // m = -inf: no key of that partial is visible to the row.
+          const float Mn = fmaxf(M, v[u].x);
+          const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+          const float wk = (v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - Mn);
+          acc = acc * a + o[u] * wk;
+          z = z * a + v[u].y * wk;
+          M = Mn;
+        }
+      }
+      if (nd.parent >= 0) {
+        // A tree slot, in the partition kernel's partial format.
+        const __amdgpu_buffer_rsrc_t wo = dev_rsrc(A.tree_o + nd.out_slot * RS * D, ostride);
+        st_dev(wo, oo, acc);
+        if (d == 0)
+          st_dev(dev_rsrc(A.tree_ml + nd.out_slot * RS * 2, mstride), om, make_float2(M, z));
+      } else {
+        const int i = row / A.group, hh = row % A.group;
+        const int h = nd.kv_head * A.group + hh;
+        const float zs = sink_log2(A, nd.seq, h);
+        const float Mx = fmaxf(M, zs);
+        const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mx);
+        const float Z = z * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
+        store_out<D, false>(A, ((int64_t)(nd.q_off + i) * A.num_q_heads + h) * D + d,
+                            acc * (a / Z));
+      }
+    }
+    if (nd.parent < 0) return;
+    node = nd.parent;
+  }
+}
+
 // The lane's query values for the FP8 MFMA: the 32 values d = 128 ks +
 // 32 c + j of its row (zeros past D), as two e4m3 terms of the row scaled by
 // a power of two, Q = qs (hi + lo). With the row's largest |value| scaled
@@ -1008,7 +1124,7 @@ constexpr int rot2(int GW) {
 // NL: loader waves per token group. CL: whether the tile waves also issue a
 // share of their group's ring loads (then P = NL + TW issuers per group,
 // else P = NL).
-template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL>
+template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL, bool FUSED>
 __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel(KernelArgs A) {
   using C = Cfg<D, FP8>;
   using RG = RingN<D, FP8, NG, OCC>;
@@ -1231,50 +1347,74 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
     ml[lane * 2 + 1] = S.l;
   }
   __syncthreads();
-  if (gp > 0 || !active) return;
-#pragma unroll
-  for (int j = 0; j < NG - 1; ++j) {
-    const f32x4* o = xo + j * kXo;
-    const float* ml = xm + (j * TW + r) * 128;
-    const float m1 = ml[lane * 2], l1 = ml[lane * 2 + 1];
-    const float M = fmaxf(S.m, m1);
-    const float a0 = (S.m == -INFINITY) ? 0.f : fast_exp2(S.m - M);
-    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) S.o[mt] = S.o[mt] * a0 + o[(r * C::MT + mt) * 64 + lane] * a1;
-    S.l = S.l * a0 + l1 * a1;
-    S.m = M;
+  const bool writer = gp == 0 && active;
+  if constexpr (!FUSED) {
+    if (!writer) return;
   }
-
-  // ---- Epilogue: the wave writes its rows (lane: row n, d = 16 mt + 4 c + i).
-  const int row = 16 * r + n;
-  if (row >= rows) return;
-  const int arow = row0 + row;  // packed row within the sequence's q x G
-  const int i = arow / G, hh = arow % G;
-  const int h = g * G + hh;
-  if (it.slot < 0) {
-    const float zs = sink_log2(A, b, h);
-    const float Mx = fmaxf(S.m, zs);
-    const float a = fast_exp2(S.m - Mx);
-    const float den = S.l * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
-    const float rs = a / den;
-    const int64_t ob = ((int64_t)(it.q_off + i) * Hq + h) * D + 4 * c;
+  if (writer) {
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) store_out<D, FP8>(A, ob + 16 * mt, S.o[mt] * rs);
-  } else {
-    // Partials go out with nontemporal stores: the reduce kernel reads them
-    // once, and lines kept out of the L2 make the kernel's final write-back
-    // shorter (the partition kernel measured 1.5 us faster on the MTP-5
-    // workload).
-    const int64_t pr = (int64_t)it.slot * A.rows_stride + arow;
+    for (int j = 0; j < NG - 1; ++j) {
+      const f32x4* o = xo + j * kXo;
+      const float* ml = xm + (j * TW + r) * 128;
+      const float m1 = ml[lane * 2], l1 = ml[lane * 2 + 1];
+      const float M = fmaxf(S.m, m1);
+      const float a0 = (S.m == -INFINITY) ? 0.f : fast_exp2(S.m - M);
+      const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-      __builtin_nontemporal_store(S.o[mt],
-                                  reinterpret_cast<f32x4*>(A.part_o + pr * D + 16 * mt + 4 * c));
-    if (c == 0) {
-      __builtin_nontemporal_store(S.m, A.part_ml + pr * 2);
-      __builtin_nontemporal_store(S.l, A.part_ml + pr * 2 + 1);
+      for (int mt = 0; mt < C::MT; ++mt)
+        S.o[mt] = S.o[mt] * a0 + o[(r * C::MT + mt) * 64 + lane] * a1;
+      S.l = S.l * a0 + l1 * a1;
+      S.m = M;
     }
+
+    // ---- Epilogue: the wave writes its rows (lane: row n, d = 16 mt +
+    // 4 c + i).
+    const int row = 16 * r + n;
+    if (row < rows) {
+      const int arow = row0 + row;  // packed row within the sequence's q x G
+      const int i = arow / G, hh = arow % G;
+      const int h = g * G + hh;
+      if (it.slot < 0) {
+        const float zs = sink_log2(A, b, h);
+        const float Mx = fmaxf(S.m, zs);
+        const float a = fast_exp2(S.m - Mx);
+        const float den = S.l * a + ((zs == -INFINITY) ? 0.f : fast_exp2(zs - Mx));
+        const float rs = a / den;
+        const int64_t ob = ((int64_t)(it.q_off + i) * Hq + h) * D + 4 * c;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt) store_out<D, FP8>(A, ob + 16 * mt, S.o[mt] * rs);
+      } else if constexpr (FUSED) {
+        // Device-scope stores: the node's last arriver may run on another XCD.
+        const int64_t RS = A.rows_stride;
+        const __amdgpu_buffer_rsrc_t wo =
+            dev_rsrc(A.part_o + it.slot * RS * D, (uint32_t)(RS * D * 4));
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+          st_dev(wo, (uint32_t)(arow * D + 16 * mt + 4 * c) * 4, S.o[mt]);
+        if (c == 0)
+          st_dev(dev_rsrc(A.part_ml + it.slot * RS * 2, (uint32_t)(RS * 8)), (uint32_t)arow * 8,
+                 make_float2(S.m, S.l));
+      } else {
+        // Partials go out with nontemporal stores: the reduce kernel reads
+        // them once, and lines kept out of the L2 make the kernel's final
+        // write-back shorter (the partition kernel measured 1.5 us faster on
+        // the MTP-5 workload).
+        const int64_t pr = (int64_t)it.slot * A.rows_stride + arow;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+          __builtin_nontemporal_store(
+              S.o[mt], reinterpret_cast<f32x4*>(A.part_o + pr * D + 16 * mt + 4 * c));
+        if (c == 0) {
+          __builtin_nontemporal_store(S.m, A.part_ml + pr * 2);
+          __builtin_nontemporal_store(S.l, A.part_ml + pr * 2 + 1);
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // Every wave of the workgroup takes part in the arrival (the pages
+    // table is no longer read: its first entry holds the arrival's flag).
+    if (it.slot >= 0) fused_arrive<D, kThreads<NG, TW, NL>>(A, it.node, &sm.pages[0]);
   }
 }
 
@@ -1436,38 +1576,49 @@ __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A
 // timing events the launch carries them itself (hipExtLaunchKernelGGL), so
 // they take the kernel's own start and end timestamps, as a kernel trace
 // does, rather than those of marker packets around its dispatch.
+template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL, bool FUSED>
+static void launch_fx(const KernelArgs& a, int n_items, hipStream_t stream, hipEvent_t ev_start,
+                      hipEvent_t ev_stop) {
+  if (ev_start && ev_stop)
+    hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL, FUSED>),
+                          dim3(n_items), dim3(kThreads<NG, TW, NL>), 0, stream, ev_start, ev_stop,
+                          0, a);
+  else
+    hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL, FUSED>), dim3(n_items),
+                       dim3(kThreads<NG, TW, NL>), 0, stream, a);
+}
 template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL>
 static void launch_one(const KernelArgs& a, int n_items, hipStream_t stream, hipEvent_t ev_start,
-                       hipEvent_t ev_stop) {
-  if (ev_start && ev_stop)
-    hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL>), dim3(n_items),
-                          dim3(kThreads<NG, TW, NL>), 0, stream, ev_start, ev_stop, 0, a);
+                       hipEvent_t ev_stop, bool fused) {
+  if (fused)
+    launch_fx<D, FP8, NG, TW, NL, OCC, CL, true>(a, n_items, stream, ev_start, ev_stop);
   else
-    hipLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL>), dim3(n_items),
-                       dim3(kThreads<NG, TW, NL>), 0, stream, a);
+    launch_fx<D, FP8, NG, TW, NL, OCC, CL, false>(a, n_items, stream, ev_start, ev_stop);
 }
 
 hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool fp8, int ntmax,
                             int occ, hipStream_t stream, hipEvent_t ev_start,
-                            hipEvent_t ev_stop) {
+                            hipEvent_t ev_stop, bool fused) {
   if (n_items <= 0) return hipSuccess;
   if (ntmax < 1 || (occ != 1 && occ != 2)) return hipErrorInvalidValue;
   if (head_dim == 256) {  // FP8 KV only, at most 48 rows; one workgroup per CU
     if (!fp8 || ntmax > 3) return hipErrorInvalidValue;
-    launch_one<256, true, 2, 3, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
+    launch_one<256, true, 2, 3, 1, 1, false>(a, n_items, stream, ev_start, ev_stop, fused);
     return hipGetLastError();
   }
   if (ntmax > 4) return hipErrorInvalidValue;
   if (fp8 && occ != 1) return hipErrorInvalidValue;  // FP8 runs one workgroup per CU
+  const hipEvent_t e0 = ev_start, e1 = ev_stop;
   if (head_dim == 128) {
-    if (fp8 && ntmax <= 3) launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
-    else if (fp8) launch_one<128, true, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
-    else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
-    else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, ev_start, ev_stop);
+    if (fp8 && ntmax <= 3)
+      launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (fp8) launch_one<128, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   } else {
-    if (fp8) launch_one<64, true, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
-    else if (occ == 1) launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, ev_start, ev_stop);
-    else launch_one<64, false, 1, 4, 1, 2, false>(a, n_items, stream, ev_start, ev_stop);
+    if (fp8) launch_one<64, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (occ == 1) launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else launch_one<64, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   }
   return hipGetLastError();
 }

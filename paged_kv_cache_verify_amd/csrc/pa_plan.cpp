@@ -76,6 +76,15 @@ struct pa_plan_s {
   ReduceItem* d_red1 = nullptr;
   float* d_l1_o = nullptr;
   float* d_l1_ml = nullptr;
+  // Fused call: merge nodes (a tree per split pair and row block), their
+  // arrival counters (zeroed once here, reset by each node's last arriver)
+  // and the tree slots the inner nodes write.
+  std::vector<MergeNode> nodes;
+  int64_t tree_slots = 0;
+  MergeNode* d_nodes = nullptr;
+  int32_t* d_counters = nullptr;
+  float* d_tree_o = nullptr;
+  float* d_tree_ml = nullptr;
   hipEvent_t ev_before = nullptr;
   hipEvent_t ev_after = nullptr;
 };
@@ -117,6 +126,14 @@ void release_device(pa_plan_s* p) {
   if (p->d_seq_rows) (void)hipFree(p->d_seq_rows);
   if (p->d_verdict_val) (void)hipFree(p->d_verdict_val);
   if (p->d_verdict_idx) (void)hipFree(p->d_verdict_idx);
+  if (p->d_nodes) (void)hipFree(p->d_nodes);
+  if (p->d_counters) (void)hipFree(p->d_counters);
+  if (p->d_tree_o) (void)hipFree(p->d_tree_o);
+  if (p->d_tree_ml) (void)hipFree(p->d_tree_ml);
+  p->d_nodes = nullptr;
+  p->d_counters = nullptr;
+  p->d_tree_o = nullptr;
+  p->d_tree_ml = nullptr;
   p->d_items = nullptr;
   p->d_tokens = nullptr;
   p->d_seq_rows = nullptr;
@@ -266,6 +283,43 @@ double auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus, int64_t& l
   return total / (3.0 * cus);
 }
 
+// The merge of one split pair's n partials in the fused call: nodes of at
+// most kFusedFanIn inputs (split evenly), level by level until one node
+// remains. Level-0 nodes take partials [first, first + count); a node of a
+// higher level takes the tree slots [first, first + count) (numbered from
+// the pair's first) that its children write, out_slot being a child's.
+struct TreeNode {
+  int32_t first, count, level;
+  int32_t out_slot;  // -1 at the root
+  int32_t parent;    // index in the tree, -1 at the root
+};
+
+void merge_tree(int32_t n, std::vector<TreeNode>& t, std::vector<int32_t>& leaf, int32_t& slots) {
+  t.clear();
+  leaf.assign(n, 0);
+  slots = 0;
+  int32_t k = (n + kFusedFanIn - 1) / kFusedFanIn, lb = 0, level = 0;
+  for (int32_t j = 0; j < k; ++j) {
+    const int32_t a = (int32_t)((int64_t)j * n / k), e = (int32_t)((int64_t)(j + 1) * n / k);
+    for (int32_t x = a; x < e; ++x) leaf[x] = (int32_t)t.size();
+    t.push_back({a, e - a, 0, -1, -1});
+  }
+  while (k > 1) {
+    const int32_t base = slots;
+    for (int32_t j = 0; j < k; ++j) t[lb + j].out_slot = base + j;
+    slots += k;
+    const int32_t k2 = (k + kFusedFanIn - 1) / kFusedFanIn, nb = (int32_t)t.size();
+    ++level;
+    for (int32_t j = 0; j < k2; ++j) {
+      const int32_t a = (int32_t)((int64_t)j * k / k2), e = (int32_t)((int64_t)(j + 1) * k / k2);
+      for (int32_t x = a; x < e; ++x) t[lb + x].parent = nb + j;
+      t.push_back({base + a, e - a, level, -1, -1});
+    }
+    lb = nb;
+    k = k2;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,7 +436,35 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
         si.slot_base = (int32_t)slots;
         slots += (int64_t)Hkv * si.n_parts;
       }
+      std::vector<TreeNode> tree;
+      std::vector<int32_t> leaf;
+      int32_t tslots = 0;
+      if (si.n_parts > 1) merge_tree(si.n_parts, tree, leaf, tslots);
       for (int g = 0; g < Hkv; ++g) {
+        // The fused call's nodes of this pair: tree node t of row block rb
+        // is node nbase + t * rblocks + rb; the pair's tree slots start at
+        // tbase (shared by the row blocks, whose rows are disjoint).
+        const int64_t nbase = (int64_t)p->nodes.size(), tbase = p->tree_slots;
+        const int32_t pslot = (int32_t)(si.slot_base + (int64_t)g * si.n_parts);
+        for (const TreeNode& tn : tree) {
+          for (int rb = 0; rb < si.rblocks; ++rb) {
+            MergeNode m{};
+            m.seq = b;
+            m.kv_head = g;
+            m.q_len = si.q_len;
+            m.q_off = si.q_off;
+            m.row0 = rb * si.rper;
+            m.nrows = std::min(si.rper, si.q_len * G - m.row0);
+            m.from_tree = tn.level > 0;
+            m.slot_base = (int32_t)(tn.level > 0 ? tbase + tn.first : pslot + tn.first);
+            m.n_parts = tn.count;
+            m.out_slot = tn.out_slot >= 0 ? (int32_t)(tbase + tn.out_slot) : -1;
+            m.parent = tn.parent >= 0 ? (int32_t)(nbase + (int64_t)tn.parent * si.rblocks + rb)
+                                      : -1;
+            p->nodes.push_back(m);
+          }
+        }
+        p->tree_slots += tslots;
         for (int k = 0; k < si.n_parts; ++k) {
           for (int rb = 0; rb < si.rblocks; ++rb) {
             WorkItem it{};
@@ -398,6 +480,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
             it.window = si.window;
             it.row0 = rb * si.rper;
             it.nrows = std::min(si.rper, si.q_len * G - it.row0);
+            it.node = si.n_parts > 1 ? (int32_t)(nbase + (int64_t)leaf[k] * si.rblocks + rb) : -1;
             p->items.push_back(it);
           }
         }
@@ -429,6 +512,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       }
     }
     if (p->items.size() >= (size_t)INT32_MAX || slots >= (int64_t)INT32_MAX ||
+        p->nodes.size() >= (size_t)INT32_MAX || p->tree_slots >= (int64_t)INT32_MAX ||
         (int64_t)p->red.size() * rows_stride * 4 >= (int64_t)INT32_MAX) {
       delete p;
       return fail(PA_E_UNSUPPORTED, "the work list exceeds a 1-D grid");
@@ -468,7 +552,8 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
         return fail(PA_E_UNSUPPORTED, "the first-level merge list exceeds a 1-D grid");
       }
     }
-    p->scratch_bytes = (slots + p->l1_slots) * rows_stride * ((int64_t)s.head_dim + 2) * 4;
+    p->scratch_bytes =
+        (slots + p->l1_slots + p->tree_slots) * rows_stride * ((int64_t)s.head_dim + 2) * 4;
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(PA_E_NOMEM, "host allocation of the work list failed");
@@ -521,6 +606,20 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     if (e == hipSuccess)
       e = hipMalloc((void**)&p->d_l1_ml, (size_t)p->l1_slots * p->rows_stride * 2 * sizeof(float));
   }
+  if (e == hipSuccess && !p->nodes.empty()) {
+    e = upload((void**)&p->d_nodes, p->nodes.data(), p->nodes.size() * sizeof(MergeNode));
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_counters, p->nodes.size() * sizeof(int32_t));
+    // The counters are zero before the plan is returned.
+    if (e == hipSuccess) e = hipMemset(p->d_counters, 0, p->nodes.size() * sizeof(int32_t));
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  }
+  if (e == hipSuccess && p->tree_slots > 0) {
+    e = hipMalloc((void**)&p->d_tree_o,
+                  (size_t)p->tree_slots * p->rows_stride * s.head_dim * sizeof(float));
+    if (e == hipSuccess)
+      e = hipMalloc((void**)&p->d_tree_ml,
+                    (size_t)p->tree_slots * p->rows_stride * 2 * sizeof(float));
+  }
   if (cur != device) (void)hipSetDevice(cur);
   if (e != hipSuccess) {
     release_device(p);
@@ -545,6 +644,14 @@ struct CallBufs {
   float* l1_ml;
 };
 
+// The fused call's buffers (the plan's own).
+struct FusedBufs {
+  const MergeNode* nodes;
+  int32_t* counters;
+  float* tree_o;
+  float* tree_ml;
+};
+
 // The argument checks every attention call makes before it launches.
 pa_status check_call(const pa_plan_t* plan, const void* q, const void* k_pool, const void* v_pool,
                      const int32_t* block_table, const float* k_scales, const float* v_scales,
@@ -563,11 +670,13 @@ pa_status check_call(const pa_plan_t* plan, const void* q, const void* k_pool, c
   return PA_OK;
 }
 
-// Enqueue the partition kernel and the reduce (one or two launches).
+// Enqueue the partition kernel and the reduce (one or two launches), or
+// (fused non-null) the fused partition kernel alone.
 pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* dev_ctx,
                       const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_table, const float* k_scales, const float* v_scales,
-                      const float* sinks, void* out, hipStream_t st) {
+                      const float* sinks, void* out, hipStream_t st,
+                      const FusedBufs* fused = nullptr) {
   const pa_shape& s = plan->shape;
   const bool fp8 = s.kv_dtype == PA_FP8_E4M3;
   KernelArgs a{};
@@ -594,6 +703,16 @@ pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* d
   a.dev_ctx = dev_ctx;
 
   hipError_t e;
+  if (fused) {
+    a.nodes = fused->nodes;
+    a.counters = fused->counters;
+    a.tree_o = fused->tree_o;
+    a.tree_ml = fused->tree_ml;
+    e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, plan->ntmax, plan->occ, st,
+                         plan->ev_before, plan->ev_after, true);
+    if (e != hipSuccess) return hip_fail(e, "fused partition kernel launch");
+    return PA_OK;
+  }
   e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, plan->ntmax, plan->occ, st,
                        plan->ev_before, plan->ev_after);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
@@ -616,7 +735,8 @@ pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* d
 
 pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, const void* k_pool,
                  const void* v_pool, const int32_t* block_table, const float* k_scales,
-                 const float* v_scales, const float* sinks, void* out, void* stream) {
+                 const float* v_scales, const float* sinks, void* out, void* stream,
+                 bool fused = false) {
   if (!plan) return fail(PA_E_INVALID, "plan is NULL");
   if (plan->device < 0) return fail(PA_E_INVALID, "a host-only plan cannot run");
   if (plan->items.empty()) return PA_OK;  // every sequence is a padded slot
@@ -624,8 +744,20 @@ pa_status decode(const pa_plan_t* plan, const int32_t* dev_ctx, const void* q, c
   if (st != PA_OK) return st;
   const CallBufs d{plan->d_items, plan->d_red,  plan->d_red1, plan->d_part_o,
                    plan->d_part_ml, plan->d_l1_o, plan->d_l1_ml};
+  const FusedBufs f{plan->d_nodes, plan->d_counters, plan->d_tree_o, plan->d_tree_ml};
   return launch_call(plan, d, dev_ctx, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
-                     out, static_cast<hipStream_t>(stream));
+                     out, static_cast<hipStream_t>(stream), fused ? &f : nullptr);
+}
+
+// Device lengths need bounds for windowed plans (see pa_decode_verify_dev).
+pa_status check_dev_lengths(const pa_plan_t* plan) {
+  if (!plan->shape.lengths_are_bounds)
+    for (const SeqInfo& si : plan->seqs)
+      if (si.q_len > 0 && si.window > 0)
+        return fail(PA_E_INVALID,
+                    "a windowed plan read with device lengths must be built with "
+                    "lengths_are_bounds = 1");
+  return PA_OK;
 }
 
 // Byte offsets of one zero-allocation call's buffers in the static scratch
@@ -666,14 +798,24 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
                                void* stream) {
   if (!plan) return fail(PA_E_INVALID, "plan is NULL");
   if (!context_lens_dev) return fail(PA_E_INVALID, "context_lens_dev is required");
-  if (!plan->shape.lengths_are_bounds)
-    for (const SeqInfo& si : plan->seqs)
-      if (si.q_len > 0 && si.window > 0)
-        return fail(PA_E_INVALID,
-                    "a windowed plan read with device lengths must be built with "
-                    "lengths_are_bounds = 1");
+  pa_status st = check_dev_lengths(plan);
+  if (st != PA_OK) return st;
   return decode(plan, context_lens_dev, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
                 out, stream);
+}
+
+pa_status pa_decode_verify_fused(const pa_plan_t* plan, const int32_t* context_lens_dev,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, const float* k_scales,
+                                 const float* v_scales, const float* sinks, void* out,
+                                 void* stream) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  if (context_lens_dev) {
+    pa_status st = check_dev_lengths(plan);
+    if (st != PA_OK) return st;
+  }
+  return decode(plan, context_lens_dev, q, k_pool, v_pool, block_table, k_scales, v_scales, sinks,
+                out, stream, true);
 }
 
 pa_status pa_decode_verify_noalloc(const pa_plan_t* plan, const void* q, const void* k_pool,

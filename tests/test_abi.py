@@ -129,6 +129,8 @@ def test_null_arguments_are_refused():
                                 None) == pav.PA_E_INVALID
     assert lib.pa_decode_verify_dev(None, None, None, None, None, None, None, None, None, None,
                                     None) == pav.PA_E_INVALID
+    assert lib.pa_decode_verify_fused(None, None, None, None, None, None, None, None, None, None,
+                                      None) == pav.PA_E_INVALID
     lib.pa_free(None)  # NULL-safe
 
 
@@ -143,6 +145,19 @@ def test_host_only_plan_refuses_to_run():
     assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
     st = pav.library().pa_verify_greedy(plan.handle, 16, pav.PA_BF16, 8, 8, 4, 4, 4, 4, None)
     assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
+    st = pav.library().pa_decode_verify_fused(plan.handle, None, 1, 1, 1, 1, None, None, None, 1,
+                                              None)
+    assert st == pav.PA_E_INVALID and "host-only" in pav.pa_last_error()
+    plan.close()
+
+
+def test_fused_call_refuses_device_lengths_on_a_windowed_plan_without_bounds():
+    """As pa_decode_verify_dev: a windowed plan read with device lengths must
+    be built on upper bounds; the refusal comes before any launch."""
+    plan = pav.pa_plan(base_shape(), [100, 50], [6, 6], [10, 0], device=-1)
+    st = pav.library().pa_decode_verify_fused(plan.handle, 8, 8, 8, 8, 8, None, None, None, 8,
+                                              None)
+    assert st == pav.PA_E_INVALID and "lengths_are_bounds" in pav.pa_last_error()
     plan.close()
 
 
@@ -221,8 +236,11 @@ def test_long_context_partitions():
     assert info["kv_bytes"] == 2 * (1 << 20) * 512
     # partials: one (rows x (D + 2)) fp32 record per item, plus the
     # first-level records of the two-level merge (more than 512 partials per
-    # pair: 2,048 fold in chunks of 64 into 32 per pair)
-    assert info["scratch_bytes"] == (info["work_items"] + 2 * 32) * 48 * (128 + 2) * 4
+    # pair: 2,048 fold in chunks of 64 into 32 per pair), plus the inner
+    # nodes' records of the single-launch call's merge tree (fan-in 16:
+    # 2,048 -> 128 -> 8 -> 1, so 128 + 8 per pair)
+    assert info["scratch_bytes"] == \
+        (info["work_items"] + 2 * 32 + 2 * (128 + 8)) * 48 * (128 + 2) * 4
     plan.close()
 
 
