@@ -64,8 +64,11 @@ def load_traffic(workload_key: str):
     return rec.get("bytes_per_launch")
 
 
-def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None, warm=False):
+def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None, warm=False,
+            fused=False):
     """Time `steps` calls on rotating pool copies; returns a dict of figures.
+    fused: time pa_decode_verify_fused (one launch; its partition kernel
+    then includes the merge) instead of the two-launch call.
 
     The timed region is one replay of a HIP graph holding the `steps` calls
     (the way a serving engine replays its decode steps), bracketed by device
@@ -111,7 +114,10 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None
 
     def call(i):
         kp, vp, ks, vs = pools[i % copies]
-        if lens_dev is None:
+        if fused:
+            pav.pa_decode_verify_fused(plan, lens_dev, dev.q, kp, vp, dev.block_table, ks, vs,
+                                       dev.sinks, out, s)
+        elif lens_dev is None:
             pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out, s)
         else:
             pav.pa_decode_verify_dev(plan, lens_dev, dev.q, kp, vp, dev.block_table, ks, vs,
@@ -175,7 +181,7 @@ def measure(wl, steps: int, warmup: int, partition_tokens=None, bound_extra=None
     # The streaming floor: the same plan's bytes through the same loads with
     # no compute (pa_stream_floor), timed the same way on the same copies.
     floor_ms = None
-    if lens_dev is None:
+    if lens_dev is None and not fused:
         with torch.cuda.stream(s):
             for i in range(steps):
                 kp, vp, ks, vs = pools[i % copies]
@@ -355,6 +361,77 @@ def spacing_study(cfg: int, partition_tokens, steps: int):
                       "host_us_per_call": res}), flush=True)
 
 
+def stamp_study(cfg: int, partition_tokens, calls: int = 8):
+    """Per-workgroup phases of the partition kernel from its stamps
+    (pa_set_workgroup_stamps), for the two-launch call and the fused call on
+    the same plan: after `calls` calls on rotating pool copies, one stamped
+    call of each. Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_verify_amd as pav
+    import workloads
+
+    wl = workloads.make(cfg)
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0, partition_tokens=partition_tokens)
+    n = plan.info()["work_items"]
+    kv = plan.info()["kv_bytes"]
+    copies = 1 if kv >= (1 << 30) else int(math.ceil((1 << 30) / kv)) + 1
+    pools = [(dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales)]
+    for _ in range(copies - 1):
+        pools.append(tuple(None if t is None else t.clone() for t in pools[0]))
+    dt = torch.float32 if wl.out_dtype == "fp32" else torch.bfloat16
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=dt, device="cuda:0")
+    st = torch.zeros((n, 8), dtype=torch.int64, device="cuda:0")
+    res = {"workload": wl.name, "work_items": n,
+           "partition_tokens": plan.info()["partition_tokens"],
+           "unit": "us from the first workgroup's start"}
+    for mode in ("two-launch", "fused"):
+        for i in range(calls + 1):
+            if i == calls:
+                st.zero_()
+                pav.pa_set_workgroup_stamps(plan, st)
+            kp, vp, ks, vs = pools[i % copies]
+            if mode == "fused":
+                pav.pa_decode_verify_fused(plan, None, dev.q, kp, vp, dev.block_table, ks, vs,
+                                           dev.sinks, out)
+            else:
+                pav.pa_decode_verify(plan, dev.q, kp, vp, dev.block_table, ks, vs, dev.sinks, out)
+            torch.cuda.synchronize()
+        pav.pa_set_workgroup_stamps(plan, None)
+        t = st.cpu().numpy()
+        T = (t[:, :7] - t[:, 0].min()) / 100.0
+        done = np.where(t[:, :7] > 0, T, -1.0).max(axis=1)  # each workgroup's last stamp
+        r = {"kernel_span_us": round(float(done.max()), 2),
+             "last_start_us": round(float(T[:, 0].max()), 2),
+             "chunk_loop_us_median": round(float(np.median(T[:, 1] - T[:, 0])), 2),
+             "chunk_loop_us_max": round(float((T[:, 1] - T[:, 0]).max()), 2),
+             "loop_end_us_max": round(float(T[:, 1].max()), 2)}
+        grid = np.arange(0.0, done.max(), 10.0)
+        r["active_workgroups_every_10us"] = [int(((T[:, 0] <= g) & (done > g)).sum()) for g in grid]
+        if mode == "fused":
+            split = t[:, 3] > 0
+            if split.any():
+                r["split_items"] = int(split.sum())
+                r["partial_stored_us_median"] = round(
+                    float(np.median((T[:, 2] - T[:, 1])[split])), 2)
+                r["arrival_us_median"] = round(float(np.median((T[:, 3] - T[:, 2])[split])), 2)
+                xcc = (t[:, 7] >> 32) & 0xF
+                for lv in range(3):
+                    m = t[:, 4 + lv] > 0
+                    if not m.any():
+                        break
+                    d = (T[:, 4 + lv] - T[:, 3 + lv])[m]
+                    r[f"level{lv}_merges"] = {
+                        "count": int(m.sum()), "us_median": round(float(np.median(d)), 2),
+                        "us_max": round(float(d.max()), 2),
+                        "per_xcc": np.bincount(xcc[m], minlength=8).tolist()}
+        res[mode] = r
+    pav.pa_free(plan)
+    print(json.dumps({"stamp_study": res}), flush=True)
+
+
 def cpu_baseline(wl, budget_s: float = 10.0):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -396,6 +473,9 @@ def main():
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--spacing", type=int, default=None,
                     help="run the back-to-back vs spaced study on this workload and exit")
+    ap.add_argument("--stamps", type=int, default=None,
+                    help="print per-workgroup phases of the two-launch and fused calls on this "
+                         "workload (with --partition-tokens) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -414,6 +494,9 @@ def main():
     torch.cuda.set_device(0)
     if args.spacing is not None:
         spacing_study(args.spacing, args.partition_tokens, min(args.steps, 40))
+        return
+    if args.stamps is not None:
+        stamp_study(args.stamps, args.partition_tokens)
         return
 
     if args.copy_calibration:
@@ -486,6 +569,19 @@ def main():
                                   / HBM_PEAK_GBS, 4),
         },
     }
+    # The same workload through the single-launch call (pa_decode_verify_fused).
+    rf = measure(wl, args.steps, args.warmup, args.partition_tokens, fused=True)
+    log(f"  single launch: wall {1e3 * rf['wall_ms_per_step']:.1f} us/step, fused partition "
+        f"kernel mean {1e3 * rf['partition_ms_mean']:.1f} us, eager "
+        f"{1e3 * rf['eager_ms_per_step']:.1f} us/step")
+    line["single_launch_call"] = {
+        "entry_point": "pa_decode_verify_fused",
+        "us_per_call": round(1e3 * rf["wall_ms_per_step"], 2),
+        "GB_s": round(rf["kv_bytes"] / (rf["wall_ms_per_step"] * 1e-3) / 1e9, 1),
+        "us_per_call_eager_launches": round(1e3 * rf["eager_ms_per_step"], 2),
+        "kernel_us_mean": round(1e3 * rf["partition_ms_mean"], 2),
+        "kernel_us_median": round(1e3 * rf["partition_ms_median"], 2),
+    }
     if args.only is None:
         # The same calls on one pool copy: the KV stays in the Infinity Cache
         # between calls, so this is not an HBM figure.
@@ -518,6 +614,12 @@ def main():
                 "work_items": rx["plan"]["work_items"],
                 "partition_tokens": rx["plan"]["partition_tokens"],
             }
+            rfx = measure(wlx, max(20, args.steps // 4), max(5, args.warmup // 4), P, fused=True)
+            log(f"  single launch: {1e3 * rfx['wall_ms_per_step']:.1f} us/call; fused kernel "
+                f"{1e3 * rfx['partition_ms_mean']:.1f} us")
+            extra[f"workload {cfg}" + ("" if P is None else f" (partition {P or 'auto'})")].update(
+                us_per_call_single_launch=round(1e3 * rfx["wall_ms_per_step"], 2),
+                single_launch_kernel_us=round(1e3 * rfx["partition_ms_mean"], 2))
             if cfg in (3,) and P is None:
                 ra = measure_append(wlx, max(50, args.steps), max(5, args.warmup // 4))
                 log(f"  kv append of the {ra['new_tokens']} new tokens (FP8 quantise): "

@@ -363,6 +363,22 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
  */
 pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
 
+/*
+ * Optional diagnostic hook: when `stamps` is non-NULL (a device buffer of
+ * 8 x work_items uint64, owned by the caller), every later attention call
+ * with this plan (pa_decode_verify, _dev, _fused, _noalloc) has each
+ * partition workgroup write, at 8 i + slot for work item i, the device's
+ * 100 MHz real-time clock at: 0 its start, 1 every wave past its chunk loop,
+ * 2 its outputs issued (for a split item of pa_decode_verify_fused: its
+ * partial's stores complete), 3 (fused, split items) its arrival counted,
+ * 4 + l (fused, l < 3) its merge of a level-l tree node done when it was the
+ * node's last arriver; slot 7 holds the XCC id in the high 32 bits and the
+ * HW_ID register (CU, SIMD, shader engine) in the low 32. Slots a
+ * workgroup does not reach are left as they were. Pass NULL to stop.
+ * Results are unchanged; the stamps cost a few stores per workgroup.
+ */
+pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,7 +3,8 @@
 The names mirror the C ABI in include/pa_verify.h (pa_plan, pa_decode_verify,
 pa_decode_verify_dev, pa_decode_verify_fused, pa_decode_verify_noalloc,
 pa_kv_append, pa_verify_greedy, pa_free, pa_last_error, pa_plan_info,
-pa_plan_items, pa_set_partition_events, pa_stream_floor). This module only
+pa_plan_items, pa_set_partition_events, pa_set_workgroup_stamps,
+pa_stream_floor). This module only
 marshals arguments: torch tensors
 are passed as raw device pointers and torch's current stream as the HIP
 stream. Every step of the computation runs in the library's HIP kernels;
@@ -26,7 +27,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_H
                 4: "PA_E_NOMEM"}
 EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_decode_verify_fused",
             "pa_decode_verify_noalloc", "pa_kv_append", "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info",
-            "pa_plan_items", "pa_set_partition_events", "pa_stream_floor")
+            "pa_plan_items", "pa_set_partition_events", "pa_set_workgroup_stamps",
+            "pa_stream_floor")
 
 
 class PaShape(ctypes.Structure):
@@ -93,6 +95,8 @@ def library() -> ctypes.CDLL:
         lib.pa_plan_items.restype = ctypes.c_int
         lib.pa_set_partition_events.argtypes = [P, P, P]
         lib.pa_set_partition_events.restype = ctypes.c_int
+        lib.pa_set_workgroup_stamps.argtypes = [P, P]
+        lib.pa_set_workgroup_stamps.restype = ctypes.c_int
         lib.pa_stream_floor.argtypes = [P, P, P, P, P, P, P]
         lib.pa_stream_floor.restype = ctypes.c_int
         _lib = lib
@@ -274,6 +278,13 @@ def pa_stream_floor(plan: Plan, k_pool, v_pool, block_table, k_scales=None, v_sc
 
 def pa_free(plan: Plan) -> None:
     plan.close()
+
+
+def pa_set_workgroup_stamps(plan: Plan, stamps=None) -> None:
+    """Attach a device int64 tensor of 8 x work_items stamps (or None to
+    stop); see pa_set_workgroup_stamps in include/pa_verify.h."""
+    plan._stamps = stamps
+    _check(library().pa_set_workgroup_stamps(plan.handle, _ptr(stamps)))
 
 
 def pa_set_partition_events(plan: Plan, before=None, after=None) -> None:

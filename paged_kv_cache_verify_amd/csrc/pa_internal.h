@@ -53,7 +53,7 @@ struct WorkItem {
 constexpr int kFusedFanIn = 16;
 
 // One merge of the fused call (single launch, no reduce kernel): n_parts
-// partials, slots [slot_base, slot_base + n_parts) of the partition
+// partials, slots slot_base + j * slot_stride (j < n_parts) of the partition
 // partials (from_tree 0) or of the tree slots (1), rows [row0, row0 + nrows)
 // of (seq, kv_head). The workgroup whose arrival brings the node's counter
 // to n_parts merges them: into the output (parent < 0), or into tree slot
@@ -70,7 +70,8 @@ struct MergeNode {
   int32_t from_tree;
   int32_t out_slot;
   int32_t parent;
-  int32_t pad[5];
+  int32_t slot_stride;
+  int32_t pad[4];
 };
 
 // A split (sequence, KV head) whose partials [slot_base, slot_base +
@@ -123,7 +124,11 @@ struct KernelArgs {
   int32_t* counters;
   float* tree_o;
   float* tree_ml;
+  // Optional per-workgroup stamps of the partition kernel (null: none):
+  // kStampsPerItem uint64 per work item, see pa_set_workgroup_stamps.
+  unsigned long long* stamps;
 };
+constexpr int kStampsPerItem = 8;
 
 // The new tokens of a verify step, for the paged KV append kernel.
 struct AppendArgs {

@@ -962,19 +962,34 @@ __device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kScopeDevice));
 }
 
+// Optional workgroup stamps (the device's 100 MHz real-time clock), taken
+// by thread 0 when the caller attached a buffer: slot 0 the workgroup's
+// start, 1 every wave past its chunk loop, 2 the outputs issued (or, for a
+// split item of the fused call, its partial's stores complete), 3 the
+// arrival counted, 4 + l the merge of tree level l done (l < 3; last
+// arrivers only), 7 the XCC id (high half) and HW_ID register (low half).
+__device__ __forceinline__ void stamp(const KernelArgs& A, int slot) {
+  if (A.stamps && threadIdx.x == 0)
+    A.stamps[(size_t)blockIdx.x * kStampsPerItem + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Arrival of a workgroup whose partial (or tree slot) is written, at merge
 // node `node`; every thread of the workgroup calls it (NT threads). The last
 // arriver resets the node's counter and folds the node's partials, row by
 // row in index order, into the output or into its tree slot, and then
 // arrives at the parent node. s_flag: one int of LDS no wave still uses.
+// (One workgroup folds a node: with device-scope loads it pulls about
+// 60 GB/s, 16 partials of 48 rows at D 128 in about 7 us, where the
+// separate reduce kernel spreads every pair's merge over the device.)
 template <int D, int NT>
 __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
   constexpr int COLS = D / 4;
   constexpr int U = 8;  // partials in flight per thread
   const int tid = threadIdx.x;
-  for (;;) {
+  for (int lev = 0;; ++lev) {
     wait_vm<0>();  // this wave's stores are complete at device scope
     __syncthreads();
+    if (lev == 0) stamp(A, 2);
     if (tid == 0) {
       const int need = A.nodes[node].n_parts;
       const int old =
@@ -985,6 +1000,7 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
         __hip_atomic_store(A.counters + node, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *s_flag = last;
     }
+    if (lev == 0) stamp(A, 3);
     __syncthreads();
     if (!*s_flag) return;  // uniform over the workgroup
     const MergeNode nd = A.nodes[node];
@@ -992,9 +1008,11 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
     const float* so = nd.from_tree ? A.tree_o : A.part_o;
     const float* sm = nd.from_tree ? A.tree_ml : A.part_ml;
     const uint32_t ostride = (uint32_t)(RS * D * 4), mstride = (uint32_t)(RS * 8);
-    const __amdgpu_buffer_rsrc_t ro = dev_rsrc(so + nd.slot_base * RS * D, ostride * nd.n_parts);
-    const __amdgpu_buffer_rsrc_t rm = dev_rsrc(sm + nd.slot_base * RS * 2, mstride * nd.n_parts);
     const int n = nd.n_parts;
+    const uint32_t span = (uint32_t)((n - 1) * nd.slot_stride + 1);  // slots the node spans
+    const __amdgpu_buffer_rsrc_t ro = dev_rsrc(so + nd.slot_base * RS * D, ostride * span);
+    const __amdgpu_buffer_rsrc_t rm = dev_rsrc(sm + nd.slot_base * RS * 2, mstride * span);
+    const uint32_t ps = ostride * nd.slot_stride, pm = mstride * nd.slot_stride;
     for (int t = tid; t < nd.nrows * COLS; t += NT) {
       const int row = nd.row0 + t / COLS;  // packed row of the sequence
       const int d = (t % COLS) * 4;
@@ -1009,8 +1027,8 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
           v[u] = make_float2(-INFINITY, 0.f);
           o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
           if (k0 + u < n) {
-            v[u] = ld_dev2(rm, om + (k0 + u) * mstride);
-            o[u] = ld_dev4(ro, oo + (k0 + u) * ostride);
+            v[u] = ld_dev2(rm, om + (k0 + u) * pm);
+            o[u] = ld_dev4(ro, oo + (k0 + u) * ps);
           }
         }
 #pragma unroll
@@ -1041,6 +1059,7 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
                             acc * (a / Z));
       }
     }
+    if (lev < 3) stamp(A, 4 + lev);
     if (nd.parent < 0) return;
     node = nd.parent;
   }
@@ -1134,6 +1153,7 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
   using SM = Smem<D, FP8, NG, TW, OCC>;
   static_assert(OCC == 1 || sizeof(SM) <= 80 * 1024, "two workgroups share a CU's LDS");
   __shared__ SM sm;
+  stamp(A, 0);
   const WorkItem it = A.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1334,6 +1354,11 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
   // loads have completed, its last wait was vmcnt(0)).
   S.l = xlane_sum4(S.l);
   __syncthreads();
+  stamp(A, 1);
+  if (A.stamps && tid == 0)
+    A.stamps[(size_t)blockIdx.x * kStampsPerItem + 7] =
+        ((unsigned long long)__builtin_amdgcn_s_getreg(0xF814) << 32) |  // XCC_ID
+        (unsigned)__builtin_amdgcn_s_getreg(0xF804);                      // HW_ID
   constexpr int kXo = TW * C::MT * 64;                              // f32x4 per group
   f32x4* xo = reinterpret_cast<f32x4*>(&sm.ring[0][0]);           // [group-1][tile][mt][lane]
   float* xm = reinterpret_cast<float*>(xo + (NG - 1) * kXo);       // [group-1][tile][lane][m, l]
@@ -1411,6 +1436,7 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
       }
     }
   }
+  if (!FUSED || it.slot < 0) stamp(A, 2);
   if constexpr (FUSED) {
     // Every wave of the workgroup takes part in the arrival (the pages
     // table is no longer read: its first entry holds the arrival's flag).
@@ -1614,10 +1640,12 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
       launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (fp8) launch_one<128, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (ntmax <= 3) launch_one<128, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
     else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   } else {
     if (fp8) launch_one<64, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (occ == 1) launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (ntmax <= 3) launch_one<64, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
     else launch_one<64, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   }
   return hipGetLastError();

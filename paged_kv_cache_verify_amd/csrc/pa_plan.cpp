@@ -87,6 +87,7 @@ struct pa_plan_s {
   float* d_tree_ml = nullptr;
   hipEvent_t ev_before = nullptr;
   hipEvent_t ev_after = nullptr;
+  unsigned long long* stamps = nullptr;  // pa_set_workgroup_stamps
 };
 
 namespace {
@@ -284,12 +285,19 @@ double auto_piece(const std::vector<SeqInfo>& seqs, int Hkv, int cus, int64_t& l
 }
 
 // The merge of one split pair's n partials in the fused call: nodes of at
-// most kFusedFanIn inputs (split evenly), level by level until one node
-// remains. Level-0 nodes take partials [first, first + count); a node of a
-// higher level takes the tree slots [first, first + count) (numbered from
-// the pair's first) that its children write, out_slot being a child's.
+// most kFusedFanIn inputs, level by level until one node remains. Level-0
+// nodes take partials first + j * stride (j < count); a node of a higher
+// level takes the tree slots [first, first + count) (numbered from the
+// pair's first) that its children write, out_slot being a child's.
+//
+// Workgroups go to the XCDs in turn (item i to XCD i mod 8), and a node is
+// merged by its last arriving item, most often its last dispatched one. A
+// leaf of 16 consecutive items would always end on the same XCD, which then
+// carries every merge; so the leaves of each run of 8 x 16 partials take
+// every L-th partial (L the run's leaves): a leaf's items share an XCD, and
+// the run's leaves spread over the eight.
 struct TreeNode {
-  int32_t first, count, level;
+  int32_t first, count, stride, level;
   int32_t out_slot;  // -1 at the root
   int32_t parent;    // index in the tree, -1 at the root
 };
@@ -298,12 +306,19 @@ void merge_tree(int32_t n, std::vector<TreeNode>& t, std::vector<int32_t>& leaf,
   t.clear();
   leaf.assign(n, 0);
   slots = 0;
-  int32_t k = (n + kFusedFanIn - 1) / kFusedFanIn, lb = 0, level = 0;
-  for (int32_t j = 0; j < k; ++j) {
-    const int32_t a = (int32_t)((int64_t)j * n / k), e = (int32_t)((int64_t)(j + 1) * n / k);
-    for (int32_t x = a; x < e; ++x) leaf[x] = (int32_t)t.size();
-    t.push_back({a, e - a, 0, -1, -1});
+  if (n <= kFusedFanIn) {
+    t.push_back({0, n, 1, 0, -1, -1});
+  } else {
+    constexpr int32_t kRun = 8 * kFusedFanIn;
+    for (int32_t b0 = 0; b0 < n; b0 += kRun) {
+      const int32_t r = std::min(kRun, n - b0), L = (r + kFusedFanIn - 1) / kFusedFanIn;
+      for (int32_t j = 0; j < L; ++j) {
+        for (int32_t x = b0 + j; x < b0 + r; x += L) leaf[x] = (int32_t)t.size();
+        t.push_back({b0 + j, (r - j + L - 1) / L, L, 0, -1, -1});
+      }
+    }
   }
+  int32_t k = (int32_t)t.size(), lb = 0, level = 0;
   while (k > 1) {
     const int32_t base = slots;
     for (int32_t j = 0; j < k; ++j) t[lb + j].out_slot = base + j;
@@ -313,7 +328,7 @@ void merge_tree(int32_t n, std::vector<TreeNode>& t, std::vector<int32_t>& leaf,
     for (int32_t j = 0; j < k2; ++j) {
       const int32_t a = (int32_t)((int64_t)j * k / k2), e = (int32_t)((int64_t)(j + 1) * k / k2);
       for (int32_t x = a; x < e; ++x) t[lb + x].parent = nb + j;
-      t.push_back({base + a, e - a, level, -1, -1});
+      t.push_back({base + a, e - a, 1, level, -1, -1});
     }
     lb = nb;
     k = k2;
@@ -458,6 +473,7 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
             m.from_tree = tn.level > 0;
             m.slot_base = (int32_t)(tn.level > 0 ? tbase + tn.first : pslot + tn.first);
             m.n_parts = tn.count;
+            m.slot_stride = tn.stride;
             m.out_slot = tn.out_slot >= 0 ? (int32_t)(tbase + tn.out_slot) : -1;
             m.parent = tn.parent >= 0 ? (int32_t)(nbase + (int64_t)tn.parent * si.rblocks + rb)
                                       : -1;
@@ -701,6 +717,7 @@ pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* d
   a.out_fp32 = s.out_dtype == PA_FP32;
   a.scale_log2 = s.softmax_scale * kLog2e;
   a.dev_ctx = dev_ctx;
+  a.stamps = plan->stamps;
 
   hipError_t e;
   if (fused) {
@@ -1013,6 +1030,12 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
     r[5] = it.row0;
     r[6] = it.nrows;
   }
+  return PA_OK;
+}
+
+pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps) {
+  if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  plan->stamps = static_cast<unsigned long long*>(stamps);
   return PA_OK;
 }
 

@@ -191,3 +191,41 @@ def test_graph_replays_with_device_lengths(P):
         ref = oracle.verify(dataclasses.replace(wl, ctx_lens=lens.clone()))[0]
         compare(f"fused replay {step} P={P}", out.float().cpu().numpy(), ref, True)
     pav.pa_free(plan)
+
+
+def test_workgroup_stamps_leave_results_unchanged_and_order_the_phases():
+    """pa_set_workgroup_stamps: with stamps attached the outputs are bit for
+    bit those without; every workgroup's start, loop end and output stamps
+    are in order; in the fused call every split item's arrival follows its
+    stored partial, and the number of workgroups that merged at tree level 0
+    equals the number of level-0 nodes (16-key items: 4,800 keys make 300
+    partials per pair in 19 leaves, 700 keys 44 in 3, 40 keys 3 in one node;
+    two KV heads)."""
+    wl = edge("stamps", ctx_lens=[4800, 700, 40], q_lens=[6, 3, 1])
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0, partition_tokens=16)
+    n = plan.info()["work_items"]
+    plain = {"two-launch": pav.run(plan, dev, out=nan_out(wl)).clone(),
+             "fused": fused(plan, dev, nan_out(wl)).clone()}
+    st = torch.zeros((n, 8), dtype=torch.int64, device="cuda:0")
+    for mode in ("two-launch", "fused"):
+        st.zero_()
+        pav.pa_set_workgroup_stamps(plan, st)
+        out = pav.run(plan, dev, out=nan_out(wl)) if mode == "two-launch" else \
+            fused(plan, dev, nan_out(wl))
+        torch.cuda.synchronize()
+        pav.pa_set_workgroup_stamps(plan, None)
+        assert torch.equal(out, plain[mode]), f"{mode}: stamps changed the results"
+        t = st.cpu().numpy()
+        assert (t[:, 0] > 0).all() and (t[:, 1] >= t[:, 0]).all() and (t[:, 2] >= t[:, 1]).all()
+        assert (t[:, 7] != 0).all()  # XCC id and HW_ID
+        items = plan.items()
+        split = np.array([it[4] >= 0 for it in items])
+        if mode == "fused":
+            assert (t[split, 3] >= t[split, 2]).all() and (t[~split, 3] == 0).all()
+            assert int((t[:, 4] > 0).sum()) == 2 * (19 + 3 + 1), "one merge per level-0 node"
+            assert int((t[:, 5] > 0).sum()) == 2 * (2 + 1), "level 1: 19 -> 2 nodes, 3 -> 1"
+            assert int((t[:, 6] > 0).sum()) == 2, "level 2: the 4,800-key pairs' roots"
+        else:
+            assert (t[:, 3:7] == 0).all()
+    pav.pa_free(plan)
