@@ -410,6 +410,22 @@ def stamp_study(cfg: int, partition_tokens, calls: int = 8):
              "loop_end_us_max": round(float(T[:, 1].max()), 2)}
         grid = np.arange(0.0, done.max(), 10.0)
         r["active_workgroups_every_10us"] = [int(((T[:, 0] <= g) & (done > g)).sum()) for g in grid]
+        # by the items' packed rows: keys, time from start to loop end, its
+        # rate, and when the class's last workgroup finished
+        items = plan.items()
+        rows = np.array([it[6] for it in items])
+        keys = np.array([it[3] - it[2] for it in items])
+        loop = T[:, 1] - T[:, 0]
+        by = {}
+        for rv in np.unique(rows):
+            m = rows == rv
+            big = m & (keys >= 512)
+            by[int(rv)] = {"items": int(m.sum()), "keys_median": int(np.median(keys[m])),
+                           "start_to_loop_end_us_median": round(float(np.median(loop[m])), 2),
+                           "ns_per_key_median": round(float(np.median(
+                               1e3 * loop[big] / keys[big])), 2) if big.any() else None,
+                           "done_us_max": round(float(done[m].max()), 2)}
+        r["by_rows"] = by
         if mode == "fused":
             split = t[:, 3] > 0
             if split.any():
