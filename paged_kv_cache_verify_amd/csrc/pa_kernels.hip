@@ -1,25 +1,27 @@
 // gfx950 kernels for paged verify attention.
 //
-// Partition kernel: one workgroup of ten waves per work item (and per CU)
-// = the keys [key_begin, key_end) of one (sequence, KV head), all q x G
-// packed rows of that KV head. The waves form two token groups of five:
-// group 0 takes the item's even 32-token chunks (two 16-token pages), group
-// 1 the odd ones, each through an LDS ring of its own that the group's
-// loader wave fills by direct global-to-LDS loads (K in MFMA A-operand
-// order, V into an XOR-swizzled token-major tile); one workgroup barrier per
-// step recycles a stage in both rings. Within a group, compute wave r owns
+// Partition kernel: one workgroup per work item (and per CU) = the keys
+// [key_begin, key_end) of one (sequence, KV head), all the item's packed
+// rows of that KV head. The waves form NG token groups (2 to 4, by layout):
+// group g takes the item's 32-token chunks (two 16-token pages) g, g + NG,
+// ..., each through an LDS ring of its own that the group's loader wave
+// fills by direct global-to-LDS loads (K as token rows with a 16-byte chunk
+// swizzle, V into an XOR-swizzled token-major tile); one workgroup barrier
+// per step recycles a stage in every ring. Within a group, compute wave r owns
 // row tile r (16 rows) and, per chunk,
-//   1. computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, tokens on the M
-//      index (FP8 codes are converted exactly to bf16 by the group's compute
-//      waves one step ahead, and the per-token K scale multiplies the
-//      scores),
-//   2. masks (causal within the query, window, key range) by selecting -inf,
+//   1. computes S^T = K Q^T, tokens on the M index: bf16 K with
+//      v_mfma_f32_16x16x32_bf16; FP8 K codes as stored with the e4m3 MFMA
+//      (v_mfma_f32_16x16x128_f8f6f4) against the query split once into two
+//      e4m3 terms, the per-token K scale multiplying the scores,
+//   2. masks (causal within the query, window, key range) by selecting -inf
+//      on boundary chunks,
 //   3. runs an online softmax in the exp2 domain whose reference max only
 //      moves when a chunk beats it by 2^8 (rare rescaling),
-//   4. accumulates O^T += V^T P^T: V^T comes from ds_read_b64_tr_b16 on
-//      the (bf16 or converted) tile, P^T straight from the S^T accumulator
-//      registers as a bf16 hi+lo pair (the per-token V scale folded in).
-// At the end the two groups' states of each tile merge through LDS and the
+//   4. accumulates O^T += V^T P^T: bf16 V^T from ds_read_b64_tr_b16 with
+//      P^T straight from the S^T accumulator registers as a bf16 hi+lo pair;
+//      FP8 V codes from ds_read_b64_tr_b8, converted exactly to fp16 in
+//      registers, against P w in fp16 (the per-token V scale folded in).
+// At the end the groups' states of each tile merge through LDS and the
 // workgroup writes the output, or this item's partial, which the reduce
 // kernel merges with the other partials of a split (sequence, KV head) by
 // log-sum-exp.
@@ -212,8 +214,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // A workgroup's layout: NG token groups of TW row-tile waves and one
 // loader each. Two groups of four tile waves serve up to 64 rows (three at
-// D 256, up to 48 rows); FP8 at D 128 with at most 48 rows uses four groups
-// of three, so that every SIMD hosts three compute waves and one loader.
+// D 256, up to 48 rows); FP8 at D 128 uses four groups of three for plans of
+// at most 48 rows and three groups of four above, so that every SIMD hosts
+// three compute waves (fifteen waves of at most 128 registers fill a SIMD's
+// 512; the two-group layout, two compute waves per SIMD, measured 4-5%
+// slower on a mixed FP8 batch).
 //
 // OCC is the number of workgroups meant to share a CU. One (OCC 1) holds
 // most of the CU's 160 KiB of LDS; that suits a plan whose items fit one
@@ -1164,7 +1169,9 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
   // every SIMD hosts three tile waves and one loader; with two groups the
   // second group's tiles 0 and 1 sit on the two SIMDs the first group's
   // tiles 0 and 1 do not use, so items of up to two tiles run one compute
-  // wave per SIMD.
+  // wave per SIMD. Three groups of five waves need no rotation: group gp's
+  // four tile waves sit on four distinct SIMDs starting at SIMD gp, so
+  // every SIMD hosts three of the twelve.
   constexpr int kRot = NG == 4 ? 1 : (NG == 2 ? rot2(GW) : 0);
   const int gp = w / GW, slot = w % GW;
   const int r = (slot + gp * kRot) % GW;
@@ -1638,7 +1645,7 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
   if (head_dim == 128) {
     if (fp8 && ntmax <= 3)
       launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, e0, e1, fused);
-    else if (fp8) launch_one<128, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (fp8) launch_one<128, true, 3, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (ntmax <= 3) launch_one<128, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
     else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);

@@ -225,14 +225,21 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
 // bound by its bytes (1). With FP8 KV a chunk costs a fixed part (its
 // streaming, the softmax's bookkeeping, the ring's barriers) plus a part
 // that grows with the busiest SIMD's compute waves per chunk, c, which
-// depends on the item's row tiles and the workgroup layout (four groups of
-// three tile waves: c = tiles / 4; two rotated groups: 1/2 for up to two
-// tiles, else 1). The slope 4/3 fits measured partition times of items with
-// two and three row tiles (about 0.5 and 0.6 us per chunk).
+// depends on the item's row tiles and the workgroup layout (head dim 128:
+// four groups of three tile waves, c = tiles / 4, for plans of at most 48
+// rows; head dims 64 and 256: two rotated groups, 1/2 for up to two tiles,
+// else 1). The slope 4/3 fits measured partition times of items with two
+// and three row tiles (about 0.5 and 0.6 us per chunk). Head dim 128 above
+// 48 rows runs three groups of four tile waves, where c = 0.22 tiles + 0.11
+// fits the measured times per key of a mixed batch's items of 1 to 4 tiles
+// (10.2, 11.1, 14.1 and 15.4 ns).
 double item_cost(const pa_shape& s, int rows, int ntmax) {
   if (s.kv_dtype != PA_FP8_E4M3) return 1.0;
   const int tiles = (rows + 15) / 16;
-  const double c = (s.head_dim == 128 && ntmax <= 3) ? 0.25 * tiles : (tiles <= 2 ? 0.5 : 1.0);
+  double c;
+  if (s.head_dim == 128 && ntmax <= 3) c = 0.25 * tiles;
+  else if (s.head_dim == 128) c = 0.22 * tiles + 0.11;
+  else c = tiles <= 2 ? 0.5 : 1.0;
   return 1.0 + (4.0 / 3.0) * c;
 }
 
@@ -533,10 +540,17 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
       delete p;
       return fail(PA_E_UNSUPPORTED, "the work list exceeds a 1-D grid");
     }
-    // Longest items first, so the short ones fill in last.
-    std::stable_sort(p->items.begin(), p->items.end(), [](const WorkItem& x, const WorkItem& y) {
-      return (x.key_end - x.key_begin) > (y.key_end - y.key_begin);
-    });
+    // Longest items first, by estimated time (keys x the sequence's cost per
+    // key), so that with more items than one round the short ones fill in
+    // last. (By keys alone, the FP8 items of many rows, fewer keys but the
+    // highest cost per key, ran in the last round of a mixed batch and set
+    // its end.)
+    const std::vector<SeqInfo>& sq = p->seqs;
+    std::stable_sort(p->items.begin(), p->items.end(),
+                     [&sq](const WorkItem& x, const WorkItem& y) {
+                       return (x.key_end - x.key_begin) * sq[x.seq].cost >
+                              (y.key_end - y.key_begin) * sq[y.seq].cost;
+                     });
     p->n_slots = slots;
     // With more than 512 partials in some pair, the pairs are merged in two
     // levels: chunks of C = ceil(n / 32) consecutive partials fold into at
