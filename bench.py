@@ -481,6 +481,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-launch", action="store_true",
+                    help="skip timing pa_decode_verify_fused (kernel traces of one path)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the FP8, long-context and mixed workloads")
     ap.add_argument("--only", type=int, default=None,
@@ -586,18 +588,19 @@ def main():
         },
     }
     # The same workload through the single-launch call (pa_decode_verify_fused).
-    rf = measure(wl, args.steps, args.warmup, args.partition_tokens, fused=True)
-    log(f"  single launch: wall {1e3 * rf['wall_ms_per_step']:.1f} us/step, fused partition "
-        f"kernel mean {1e3 * rf['partition_ms_mean']:.1f} us, eager "
-        f"{1e3 * rf['eager_ms_per_step']:.1f} us/step")
-    line["single_launch_call"] = {
-        "entry_point": "pa_decode_verify_fused",
-        "us_per_call": round(1e3 * rf["wall_ms_per_step"], 2),
-        "GB_s": round(rf["kv_bytes"] / (rf["wall_ms_per_step"] * 1e-3) / 1e9, 1),
-        "us_per_call_eager_launches": round(1e3 * rf["eager_ms_per_step"], 2),
-        "kernel_us_mean": round(1e3 * rf["partition_ms_mean"], 2),
-        "kernel_us_median": round(1e3 * rf["partition_ms_median"], 2),
-    }
+    if not args.no_single_launch:
+        rf = measure(wl, args.steps, args.warmup, args.partition_tokens, fused=True)
+        log(f"  single launch: wall {1e3 * rf['wall_ms_per_step']:.1f} us/step, fused partition "
+            f"kernel mean {1e3 * rf['partition_ms_mean']:.1f} us, eager "
+            f"{1e3 * rf['eager_ms_per_step']:.1f} us/step")
+        line["single_launch_call"] = {
+            "entry_point": "pa_decode_verify_fused",
+            "us_per_call": round(1e3 * rf["wall_ms_per_step"], 2),
+            "GB_s": round(rf["kv_bytes"] / (rf["wall_ms_per_step"] * 1e-3) / 1e9, 1),
+            "us_per_call_eager_launches": round(1e3 * rf["eager_ms_per_step"], 2),
+            "kernel_us_mean": round(1e3 * rf["partition_ms_mean"], 2),
+            "kernel_us_median": round(1e3 * rf["partition_ms_median"], 2),
+        }
     if args.only is None:
         # The same calls on one pool copy: the KV stays in the Infinity Cache
         # between calls, so this is not an HBM figure.
