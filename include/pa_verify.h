@@ -365,7 +365,9 @@ pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
 
 /*
  * Optional diagnostic hook: when `stamps` is non-NULL (a device buffer of
- * 8 x work_items uint64, owned by the caller), every later attention call
+ * `capacity` uint64, owned by the caller, at least 8 x work_items of the
+ * plan: PA_E_INVALID otherwise, and the hook is left as it was), every later
+ * attention call
  * with this plan (pa_decode_verify, _dev, _fused, _noalloc) has each
  * partition workgroup write, at 8 i + slot for work item i, the device's
  * 100 MHz real-time clock at: 0 its start, 1 every wave past its chunk loop,
@@ -377,7 +379,7 @@ pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
  * workgroup does not reach are left as they were. Pass NULL to stop.
  * Results are unchanged; the stamps cost a few stores per workgroup.
  */
-pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps);
+pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps, int64_t capacity);
 
 #ifdef __cplusplus
 }

@@ -95,7 +95,7 @@ def library() -> ctypes.CDLL:
         lib.pa_plan_items.restype = ctypes.c_int
         lib.pa_set_partition_events.argtypes = [P, P, P]
         lib.pa_set_partition_events.restype = ctypes.c_int
-        lib.pa_set_workgroup_stamps.argtypes = [P, P]
+        lib.pa_set_workgroup_stamps.argtypes = [P, P, ctypes.c_int64]
         lib.pa_set_workgroup_stamps.restype = ctypes.c_int
         lib.pa_stream_floor.argtypes = [P, P, P, P, P, P, P]
         lib.pa_stream_floor.restype = ctypes.c_int
@@ -281,10 +281,15 @@ def pa_free(plan: Plan) -> None:
 
 
 def pa_set_workgroup_stamps(plan: Plan, stamps=None) -> None:
-    """Attach a device int64 tensor of 8 x work_items stamps (or None to
-    stop); see pa_set_workgroup_stamps in include/pa_verify.h."""
+    """Attach a device int64 tensor of at least 8 x work_items stamps (or None
+    to stop); see pa_set_workgroup_stamps in include/pa_verify.h."""
+    import torch
+
+    if stamps is not None and stamps.dtype != torch.int64:
+        raise ValueError("stamps must be an int64 tensor")
+    cap = 0 if stamps is None else stamps.numel()
+    _check(library().pa_set_workgroup_stamps(plan.handle, _ptr(stamps), cap))
     plan._stamps = stamps
-    _check(library().pa_set_workgroup_stamps(plan.handle, _ptr(stamps)))
 
 
 def pa_set_partition_events(plan: Plan, before=None, after=None) -> None:

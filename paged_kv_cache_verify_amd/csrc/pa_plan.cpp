@@ -1047,8 +1047,12 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
   return PA_OK;
 }
 
-pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps) {
+pa_status pa_set_workgroup_stamps(pa_plan_t* plan, void* stamps, int64_t capacity) {
   if (!plan) return fail(PA_E_INVALID, "plan is NULL");
+  const int64_t need = (int64_t)kStampsPerItem * (int64_t)plan->items.size();
+  if (stamps && capacity < need)
+    return fail(PA_E_INVALID, "the stamps buffer holds %lld entries; the plan's %zu work items "
+                "need %lld", (long long)capacity, plan->items.size(), (long long)need);
   plan->stamps = static_cast<unsigned long long*>(stamps);
   return PA_OK;
 }

@@ -151,6 +151,20 @@ def test_host_only_plan_refuses_to_run():
     plan.close()
 
 
+def test_workgroup_stamps_refuse_a_buffer_smaller_than_the_work_list():
+    """The stamp hook checks the buffer's capacity (8 per work item) before
+    it is attached; NULL always detaches."""
+    plan = pav.pa_plan(base_shape(partition_tokens=16), [100, 50], [6, 6], None, device=-1)
+    n = plan.info()["work_items"]
+    lib = pav.library()
+    st = lib.pa_set_workgroup_stamps(plan.handle, 64, 8 * n - 1)
+    assert st == pav.PA_E_INVALID and "stamps buffer" in pav.pa_last_error()
+    assert lib.pa_set_workgroup_stamps(plan.handle, 64, 8 * n) == pav.PA_OK
+    assert lib.pa_set_workgroup_stamps(plan.handle, None, 0) == pav.PA_OK
+    assert lib.pa_set_workgroup_stamps(None, None, 0) == pav.PA_E_INVALID
+    plan.close()
+
+
 def test_fused_call_refuses_device_lengths_on_a_windowed_plan_without_bounds():
     """As pa_decode_verify_dev: a windowed plan read with device lengths must
     be built on upper bounds; the refusal comes before any launch."""
