@@ -177,9 +177,11 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
                                void* stream);
 
 /*
- * The verify-attention call as a single launch: the partition kernel merges
- * the partial results of every split (sequence, KV head) itself, and no
- * reduce kernel follows. Source: ATOM #3091 ("High-interactivity monokernel
+ * The verify-attention call as a single persistent launch: a grid of at most
+ * the device's resident workgroups takes the plan's work items in turn (each
+ * workgroup starts with its own and fetches the next from a device counter),
+ * and the partition kernel merges the partial results of every split
+ * (sequence, KV head) itself, so no reduce kernel follows. Source: ATOM #3091 ("High-interactivity monokernel
  * decode for DeepSeek-V4.1-Flash on MI355X", Summary: a decode layer runs as
  * one persistent kernel; How to reproduce: full graph capture); ATOM #2843
  * ("keep MTP-5 decode on FlyDSL pa_decode past the gluon query-length
@@ -195,8 +197,9 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
  * merges that node's partials: into the output at the root, else into an
  * input of the parent node, where it arrives in turn. The counters are
  * part of the plan's device memory, zero when pa_plan returns and reset by
- * each node's last arriver, so every call leaves them at zero (graph replays
- * included). Calls with one plan that overlap on the device (different
+ * each node's last arriver (the work-list counters by the last workgroup to
+ * finish), so every call leaves them at zero (graph replays included). No
+ * workgroup ever waits for another. Calls with one plan that overlap on the device (different
  * streams or threads) race on the counters and partials and must be
  * serialised by the caller. Results are pa_decode_verify's up to the order
  * of the log-sum-exp merge (float rounding). Otherwise as pa_decode_verify:

@@ -124,6 +124,12 @@ struct KernelArgs {
   int32_t* counters;
   float* tree_o;
   float* tree_ml;
+  // Fused call's persistent grid: the work list's length, the grid (at most
+  // the device's resident workgroups) and two counters, zero between calls
+  // (the next item to take; the workgroups done).
+  int32_t n_items;
+  int32_t grid;
+  int32_t* work;
   // Optional per-workgroup stamps of the partition kernel (null: none):
   // kStampsPerItem uint64 per work item, see pa_set_workgroup_stamps.
   unsigned long long* stamps;

@@ -277,6 +277,7 @@ template <int D, bool FP8, int NG, int TW, int OCC>
 struct Smem {
   alignas(1024) unsigned char ring[NG][RingN<D, FP8, NG, OCC>::RING];
   int32_t pages[2 * kMaxItemChunks];  // page ids of each chunk's two pages
+  int32_t next_item;                  // single-launch call: the workgroup's next item
 };
 
 #define PAV_LDS_VOID __attribute__((address_space(3))) void
@@ -967,15 +968,15 @@ __device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kScopeDevice));
 }
 
-// Optional workgroup stamps (the device's 100 MHz real-time clock), taken
-// by thread 0 when the caller attached a buffer: slot 0 the workgroup's
-// start, 1 every wave past its chunk loop, 2 the outputs issued (or, for a
+// Optional stamps per work item (the device's 100 MHz real-time clock),
+// taken by thread 0 of the workgroup running it when the caller attached a
+// buffer: slot 0 the item's start, 1 every wave past its chunk loop, 2 the outputs issued (or, for a
 // split item of the fused call, its partial's stores complete), 3 the
 // arrival counted, 4 + l the merge of tree level l done (l < 3; last
 // arrivers only), 7 the XCC id (high half) and HW_ID register (low half).
-__device__ __forceinline__ void stamp(const KernelArgs& A, int slot) {
+__device__ __forceinline__ void stamp(const KernelArgs& A, int item, int slot) {
   if (A.stamps && threadIdx.x == 0)
-    A.stamps[(size_t)blockIdx.x * kStampsPerItem + slot] = __builtin_amdgcn_s_memrealtime();
+    A.stamps[(size_t)item * kStampsPerItem + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Arrival of a workgroup whose partial (or tree slot) is written, at merge
@@ -987,14 +988,14 @@ __device__ __forceinline__ void stamp(const KernelArgs& A, int slot) {
 // 60 GB/s, 16 partials of 48 rows at D 128 in about 7 us, where the
 // separate reduce kernel spreads every pair's merge over the device.)
 template <int D, int NT>
-__device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
+__device__ void fused_arrive(const KernelArgs& A, int item, int node, int* s_flag) {
   constexpr int COLS = D / 4;
   constexpr int U = 8;  // partials in flight per thread
   const int tid = threadIdx.x;
   for (int lev = 0;; ++lev) {
     wait_vm<0>();  // this wave's stores are complete at device scope
     __syncthreads();
-    if (lev == 0) stamp(A, 2);
+    if (lev == 0) stamp(A, item, 2);
     if (tid == 0) {
       const int need = A.nodes[node].n_parts;
       const int old =
@@ -1005,7 +1006,7 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
         __hip_atomic_store(A.counters + node, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *s_flag = last;
     }
-    if (lev == 0) stamp(A, 3);
+    if (lev == 0) stamp(A, item, 3);
     __syncthreads();
     if (!*s_flag) return;  // uniform over the workgroup
     const MergeNode nd = A.nodes[node];
@@ -1064,7 +1065,7 @@ __device__ void fused_arrive(const KernelArgs& A, int node, int* s_flag) {
                             acc * (a / Z));
       }
     }
-    if (lev < 3) stamp(A, 4 + lev);
+    if (lev < 3) stamp(A, item, 4 + lev);
     if (nd.parent < 0) return;
     node = nd.parent;
   }
@@ -1148,18 +1149,19 @@ constexpr int rot2(int GW) {
 // NL: loader waves per token group. CL: whether the tile waves also issue a
 // share of their group's ring loads (then P = NL + TW issuers per group,
 // else P = NL).
+// One work item, by the whole workgroup: item `idx` of the list. FUSED:
+// the item of the single-launch call, which also fetches the index of the
+// workgroup's next item (sm.next_item, set by thread 0 at the end).
 template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL, bool FUSED>
-__global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel(KernelArgs A) {
+__device__ __forceinline__ void partition_item(const KernelArgs& A,
+                                               Smem<D, FP8, NG, TW, OCC>& sm, int idx) {
   using C = Cfg<D, FP8>;
   using RG = RingN<D, FP8, NG, OCC>;
   constexpr int GW = TW + NL;            // waves per group
   constexpr int P = NL + (CL ? TW : 0);  // load issuers per group
   using SH = Share<RG::T, P>;
-  using SM = Smem<D, FP8, NG, TW, OCC>;
-  static_assert(OCC == 1 || sizeof(SM) <= 80 * 1024, "two workgroups share a CU's LDS");
-  __shared__ SM sm;
-  stamp(A, 0);
-  const WorkItem it = A.items[blockIdx.x];
+  stamp(A, idx, 0);
+  const WorkItem it = A.items[idx];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -1283,6 +1285,15 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unbounded
   }
   ring_barrier();  // the page table is visible to every wave
+  // The single-launch call's next item for this workgroup, fetched now so
+  // that the round trip overlaps the item (the query loads above are done;
+  // no other wait of this wave covers vector memory until the epilogue).
+  int next_item = 0;
+  if constexpr (FUSED) {
+    if (tid == 0)
+      next_item = (int)gridDim.x +
+                  __hip_atomic_fetch_add(A.work, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const uint32_t pages_addr = lds_addr(sm.pages);
   unsigned char* ring = sm.ring[gp];
 
@@ -1361,9 +1372,9 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
   // loads have completed, its last wait was vmcnt(0)).
   S.l = xlane_sum4(S.l);
   __syncthreads();
-  stamp(A, 1);
+  stamp(A, idx, 1);
   if (A.stamps && tid == 0)
-    A.stamps[(size_t)blockIdx.x * kStampsPerItem + 7] =
+    A.stamps[(size_t)idx * kStampsPerItem + 7] =
         ((unsigned long long)__builtin_amdgcn_s_getreg(0xF814) << 32) |  // XCC_ID
         (unsigned)__builtin_amdgcn_s_getreg(0xF804);                      // HW_ID
   constexpr int kXo = TW * C::MT * 64;                              // f32x4 per group
@@ -1443,11 +1454,47 @@ __global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel
       }
     }
   }
-  if (!FUSED || it.slot < 0) stamp(A, 2);
+  if (!FUSED || it.slot < 0) stamp(A, idx, 2);
   if constexpr (FUSED) {
     // Every wave of the workgroup takes part in the arrival (the pages
     // table is no longer read: its first entry holds the arrival's flag).
-    if (it.slot >= 0) fused_arrive<D, kThreads<NG, TW, NL>>(A, it.node, &sm.pages[0]);
+    if (it.slot >= 0) fused_arrive<D, kThreads<NG, TW, NL>>(A, idx, it.node, &sm.pages[0]);
+    if (tid == 0) sm.next_item = next_item;
+  }
+}
+
+// The partition kernel. Two-launch call: one workgroup per work item.
+// Single-launch call (FUSED): a persistent grid of at most the device's
+// resident workgroups; workgroup w runs item w, then the items it takes in
+// turn from the counter A.work[0] (item gridDim.x + the count), until the
+// list is exhausted. No workgroup waits for another, so the grid need not
+// all be resident. Each workgroup ends by adding one to A.work[1]; the
+// last one resets both counters, as every workgroup has then made its last
+// fetch, so the next call (or graph replay) starts from zero.
+template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL, bool FUSED>
+__global__ __launch_bounds__((kThreads<NG, TW, NL>), 1) void pa_partition_kernel(KernelArgs A) {
+  using SM = Smem<D, FP8, NG, TW, OCC>;
+  static_assert(OCC == 1 || sizeof(SM) <= 80 * 1024, "two workgroups share a CU's LDS");
+  __shared__ SM sm;
+  if constexpr (!FUSED) {
+    partition_item<D, FP8, NG, TW, NL, OCC, CL, false>(A, sm, blockIdx.x);
+  } else {
+    int idx = blockIdx.x;
+    while (idx < A.n_items) {  // uniform over the workgroup
+      partition_item<D, FP8, NG, TW, NL, OCC, CL, true>(A, sm, idx);
+      // Every wave is done with the item's LDS (and reads the next index)
+      // before the next item's loads and page table overwrite it.
+      __syncthreads();
+      idx = sm.next_item;
+    }
+    if (threadIdx.x == 0) {
+      const int done =
+          __hip_atomic_fetch_add(A.work + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (int)gridDim.x - 1) {
+        __hip_atomic_store(A.work, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(A.work + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -1612,6 +1659,9 @@ __global__ __launch_bounds__(RB * D / 4) void pa_reduce_rows_kernel(KernelArgs A
 template <int D, bool FP8, int NG, int TW, int NL, int OCC, bool CL, bool FUSED>
 static void launch_fx(const KernelArgs& a, int n_items, hipStream_t stream, hipEvent_t ev_start,
                       hipEvent_t ev_stop) {
+  // The single-launch call's persistent grid: at most the resident
+  // workgroups (a.grid, from the plan), at most the items.
+  if (FUSED) n_items = n_items < a.grid ? n_items : a.grid;
   if (ev_start && ev_stop)
     hipExtLaunchKernelGGL((pa_partition_kernel<D, FP8, NG, TW, NL, OCC, CL, FUSED>),
                           dim3(n_items), dim3(kThreads<NG, TW, NL>), 0, stream, ev_start, ev_stop,

@@ -77,8 +77,9 @@ struct pa_plan_s {
   float* d_l1_o = nullptr;
   float* d_l1_ml = nullptr;
   // Fused call: merge nodes (a tree per split pair and row block), their
-  // arrival counters (zeroed once here, reset by each node's last arriver)
-  // and the tree slots the inner nodes write.
+  // arrival counters (zeroed once here, reset by each node's last arriver;
+  // two more after them for the persistent grid's work list) and the tree
+  // slots the inner nodes write.
   std::vector<MergeNode> nodes;
   int64_t tree_slots = 0;
   MergeNode* d_nodes = nullptr;
@@ -636,11 +637,13 @@ pa_status pa_plan(const pa_shape* shape, const int32_t* context_lens, const int3
     if (e == hipSuccess)
       e = hipMalloc((void**)&p->d_l1_ml, (size_t)p->l1_slots * p->rows_stride * 2 * sizeof(float));
   }
-  if (e == hipSuccess && !p->nodes.empty()) {
+  if (e == hipSuccess)
     e = upload((void**)&p->d_nodes, p->nodes.data(), p->nodes.size() * sizeof(MergeNode));
-    if (e == hipSuccess) e = hipMalloc((void**)&p->d_counters, p->nodes.size() * sizeof(int32_t));
+  if (e == hipSuccess) {
+    const size_t nc = (p->nodes.size() + 2) * sizeof(int32_t);
+    e = hipMalloc((void**)&p->d_counters, nc);
     // The counters are zero before the plan is returned.
-    if (e == hipSuccess) e = hipMemset(p->d_counters, 0, p->nodes.size() * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(p->d_counters, 0, nc);
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   }
   if (e == hipSuccess && p->tree_slots > 0) {
@@ -739,6 +742,9 @@ pa_status launch_call(const pa_plan_t* plan, const CallBufs& d, const int32_t* d
     a.counters = fused->counters;
     a.tree_o = fused->tree_o;
     a.tree_ml = fused->tree_ml;
+    a.n_items = (int32_t)plan->items.size();
+    a.grid = plan->cus * plan->occ;
+    a.work = fused->counters + plan->nodes.size();
     e = launch_partition(a, (int)plan->items.size(), s.head_dim, fp8, plan->ntmax, plan->occ, st,
                          plan->ev_before, plan->ev_after, true);
     if (e != hipSuccess) return hip_fail(e, "fused partition kernel launch");
