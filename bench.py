@@ -538,7 +538,8 @@ def main():
         f"{1e3 * r['event_ms_per_step']:.1f} us/step, partition kernel mean "
         f"{1e3 * r['partition_ms_mean']:.1f} us (median {1e3 * r['partition_ms_median']:.1f}, "
         f"p90 {1e3 * r['partition_ms_p90']:.1f}) = {achieved:.0f} GB/s, eager "
-        f"{1e3 * r['eager_ms_per_step']:.1f} us/step; stream floor {1e3 * r['floor_ms_mean']:.1f} us; "
+        f"{1e3 * r['eager_ms_per_step']:.1f} us/step; stream floor "
+        f"{1e3 * r['floor_ms_mean']:.1f} us; "
         f"plan {r['plan']}, {r['copies']} pool copies")
 
     key = f"workload{main_cfg}"

@@ -181,9 +181,10 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
  * the device's resident workgroups takes the plan's work items in turn (each
  * workgroup starts with its own and fetches the next from a device counter),
  * and the partition kernel merges the partial results of every split
- * (sequence, KV head) itself, so no reduce kernel follows. Source: ATOM #3091 ("High-interactivity monokernel
- * decode for DeepSeek-V4.1-Flash on MI355X", Summary: a decode layer runs as
- * one persistent kernel; How to reproduce: full graph capture); ATOM #2843
+ * (sequence, KV head) itself, so no reduce kernel follows. Source: ATOM
+ * #3091 ("High-interactivity monokernel decode for DeepSeek-V4.1-Flash on
+ * MI355X", Summary: a decode layer runs as one persistent kernel; How to
+ * reproduce: full graph capture); ATOM #2843
  * ("keep MTP-5 decode on FlyDSL pa_decode past the gluon query-length
  * limit", Change: persistent and non-persistent decode calls are routed
  * apart).
@@ -199,9 +200,9 @@ pa_status pa_decode_verify_dev(const pa_plan_t* plan, const int32_t* context_len
  * part of the plan's device memory, zero when pa_plan returns and reset by
  * each node's last arriver (the work-list counters by the last workgroup to
  * finish), so every call leaves them at zero (graph replays included). No
- * workgroup ever waits for another. Calls with one plan that overlap on the device (different
- * streams or threads) race on the counters and partials and must be
- * serialised by the caller. Results are pa_decode_verify's up to the order
+ * workgroup ever waits for another. Calls with one plan that overlap on the
+ * device (different streams or threads) race on the counters and partials
+ * and must be serialised by the caller. Results are pa_decode_verify's up to the order
  * of the log-sum-exp merge (float rounding). Otherwise as pa_decode_verify:
  * asynchronous, allocation-free, graph-capturable, the same errors (and
  * PA_E_INVALID for a windowed plan read with device lengths unless it was
@@ -361,8 +362,9 @@ pa_status pa_plan_items(const pa_plan_t* plan, int32_t* items, int32_t capacity)
  * plan's device), every later pa_decode_verify launches the partition kernel
  * (and pa_stream_floor its kernel) with the two events attached
  * (hipExtLaunchKernelGGL), so `before` and `after` take that kernel's own
- * start and end timestamps on the call's stream. Pass NULLs to stop (a call to be captured in a graph should run
- * without them). Timing is the only effect; results are unchanged.
+ * start and end timestamps on the call's stream. Pass NULLs to stop (a call
+ * to be captured in a graph should run without them). Timing is the only
+ * effect; results are unchanged.
  */
 pa_status pa_set_partition_events(pa_plan_t* plan, void* before, void* after);
 

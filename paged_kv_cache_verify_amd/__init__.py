@@ -26,9 +26,9 @@ ITEM_FIELDS = 7  # int32 per work item from pa_plan_items
 STATUS_NAMES = {0: "PA_OK", 1: "PA_E_INVALID", 2: "PA_E_UNSUPPORTED", 3: "PA_E_HIP",
                 4: "PA_E_NOMEM"}
 EXPORTED = ("pa_plan", "pa_decode_verify", "pa_decode_verify_dev", "pa_decode_verify_fused",
-            "pa_decode_verify_noalloc", "pa_kv_append", "pa_verify_greedy", "pa_free", "pa_last_error", "pa_plan_info",
-            "pa_plan_items", "pa_set_partition_events", "pa_set_workgroup_stamps",
-            "pa_stream_floor")
+            "pa_decode_verify_noalloc", "pa_kv_append", "pa_verify_greedy", "pa_free",
+            "pa_last_error", "pa_plan_info", "pa_plan_items", "pa_set_partition_events",
+            "pa_set_workgroup_stamps", "pa_stream_floor")
 
 
 class PaShape(ctypes.Structure):

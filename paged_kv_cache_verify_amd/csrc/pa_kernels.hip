@@ -970,10 +970,11 @@ __device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 // Optional stamps per work item (the device's 100 MHz real-time clock),
 // taken by thread 0 of the workgroup running it when the caller attached a
-// buffer: slot 0 the item's start, 1 every wave past its chunk loop, 2 the outputs issued (or, for a
-// split item of the fused call, its partial's stores complete), 3 the
-// arrival counted, 4 + l the merge of tree level l done (l < 3; last
-// arrivers only), 7 the XCC id (high half) and HW_ID register (low half).
+// buffer: slot 0 the item's start, 1 every wave past its chunk loop, 2 the
+// outputs issued (or, for a split item of the fused call, its partial's
+// stores complete), 3 the arrival counted, 4 + l the merge of tree level l
+// done (l < 3; last arrivers only), 7 the XCC id (high half) and HW_ID
+// register (low half).
 __device__ __forceinline__ void stamp(const KernelArgs& A, int item, int slot) {
   if (A.stamps && threadIdx.x == 0)
     A.stamps[(size_t)item * kStampsPerItem + slot] = __builtin_amdgcn_s_memrealtime();
@@ -1696,13 +1697,17 @@ hipError_t launch_partition(const KernelArgs& a, int n_items, int head_dim, bool
     if (fp8 && ntmax <= 3)
       launch_one<128, true, 4, 3, 1, 1, false>(a, n_items, stream, e0, e1, fused);
     else if (fp8) launch_one<128, true, 3, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
-    else if (occ == 1) launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
-    else if (ntmax <= 3) launch_one<128, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
+    else if (occ == 1)
+      launch_one<128, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (ntmax <= 3)
+      launch_one<128, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
     else launch_one<128, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   } else {
     if (fp8) launch_one<64, true, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
-    else if (occ == 1) launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
-    else if (ntmax <= 3) launch_one<64, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
+    else if (occ == 1)
+      launch_one<64, false, 2, 4, 1, 1, false>(a, n_items, stream, e0, e1, fused);
+    else if (ntmax <= 3)
+      launch_one<64, false, 1, 3, 1, 2, false>(a, n_items, stream, e0, e1, fused);
     else launch_one<64, false, 1, 4, 1, 2, false>(a, n_items, stream, e0, e1, fused);
   }
   return hipGetLastError();

@@ -86,11 +86,12 @@ hipError_t launch_stream_floor(const KernelArgs& a, int n_items, int head_dim, b
                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (n_items <= 0) return hipSuccess;
   // Template argument: bytes per token row of a page (D x element size).
-  if (fp8 && head_dim == 256) launch_floor_one<256, true>(a, n_items, stream, ev_start, ev_stop);
-  else if (fp8 && head_dim == 128) launch_floor_one<128, true>(a, n_items, stream, ev_start, ev_stop);
-  else if (fp8 && head_dim == 64) launch_floor_one<64, true>(a, n_items, stream, ev_start, ev_stop);
-  else if (!fp8 && head_dim == 128) launch_floor_one<256, false>(a, n_items, stream, ev_start, ev_stop);
-  else if (!fp8 && head_dim == 64) launch_floor_one<128, false>(a, n_items, stream, ev_start, ev_stop);
+  const hipEvent_t e0 = ev_start, e1 = ev_stop;
+  if (fp8 && head_dim == 256) launch_floor_one<256, true>(a, n_items, stream, e0, e1);
+  else if (fp8 && head_dim == 128) launch_floor_one<128, true>(a, n_items, stream, e0, e1);
+  else if (fp8 && head_dim == 64) launch_floor_one<64, true>(a, n_items, stream, e0, e1);
+  else if (!fp8 && head_dim == 128) launch_floor_one<256, false>(a, n_items, stream, e0, e1);
+  else if (!fp8 && head_dim == 64) launch_floor_one<128, false>(a, n_items, stream, e0, e1);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
