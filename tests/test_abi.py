@@ -151,6 +151,26 @@ def test_host_only_plan_refuses_to_run():
     plan.close()
 
 
+# The single-launch call's merge trees, seen through the plan's scratch: one
+# pair (1 KV head, q 6 x G 8 = 48 rows) of n 16-key partials keeps n
+# partition partials plus one tree slot per inner node. Nodes take at most
+# 16 inputs; the leaves cover runs of 128 partials (ceil(r / 16) leaves per
+# run of r), and each level above groups at most 16 nodes. Expected inner
+# nodes: 16 -> 0 (one node); 17 -> 2 leaves; 128 -> 8; 129 -> 8 + 1;
+# 256 -> 16; 257 -> 17 leaves + 2 on level 1; 300 -> 8 + 8 + 3 = 19 leaves
+# + 2; 512 -> 32 leaves + 2.
+@pytest.mark.parametrize("n,inner", [(16, 0), (17, 2), (128, 8), (129, 9), (256, 16),
+                                     (257, 19), (300, 21), (512, 34)])
+def test_fused_merge_tree_slots(n, inner):
+    shape = base_shape(num_seqs=1, num_q_heads=8, num_kv_heads=1, partition_tokens=16,
+                       max_blocks_per_seq=600, num_blocks=1200)
+    plan = pav.pa_plan(shape, [16 * n], [6], None, device=-1)
+    info = plan.info()
+    assert info["work_items"] == n
+    assert info["scratch_bytes"] == (n + inner) * 48 * (128 + 2) * 4
+    plan.close()
+
+
 def test_workgroup_stamps_refuse_a_buffer_smaller_than_the_work_list():
     """The stamp hook checks the buffer's capacity (8 per work item) before
     it is attached; NULL always detaches."""
