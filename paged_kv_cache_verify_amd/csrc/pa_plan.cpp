@@ -220,8 +220,6 @@ pa_status validate(const pa_shape* s, const int32_t* ctx, const int32_t* ql, con
   return PA_OK;
 }
 
-// Work items of (at most) `piece` keys for every active sequence, counted
-// over all KV heads.
 // Relative time per key of an item with `rows` packed rows. bf16 KV is
 // bound by its bytes (1). With FP8 KV a chunk costs a fixed part (its
 // streaming, the softmax's bookkeeping, the ring's barriers) plus a part
@@ -251,6 +249,8 @@ int64_t keys_for(double P, double cost, int64_t lo_keys) {
   return std::min<int64_t>(kMaxItemKeys, std::max<int64_t>(lo_keys, k));
 }
 
+// Work items of a cost-weighted item size P for every active sequence,
+// counted over all KV heads and row blocks.
 int64_t count_items(const std::vector<SeqInfo>& seqs, int Hkv, double P, int64_t lo_keys) {
   int64_t n = 0;
   for (const SeqInfo& si : seqs) {
