@@ -327,6 +327,45 @@ def test_random_sweep(case):
           partition_tokens=P)
 
 
+# Larger random batches: 8 to 39 sequences with contexts up to 40,000 keys
+# (plans of several rounds, two workgroups per CU for bf16, thousands of
+# items at the small partition sizes, two-level merges), through the
+# two-launch call and the single-launch call, both against one oracle run.
+def _random_batch_case(rng):
+    kw, P = _random_case(rng)
+    B = int(rng.integers(8, 40))
+    G = kw["num_q_heads"] // kw["num_kv_heads"]
+    q = [int(rng.integers(0, min(8, 128 // G) + 1)) for _ in range(B)]
+    q[0] = max(q[0], 1)
+    kw["q_lens"] = q
+    kw["ctx_lens"] = [max(qb, 1) + int(rng.integers(0, 40000)) for qb in q]
+    for k in ("window", "sinks_rows"):
+        if k in kw:
+            kw[k] = (kw[k] * B)[:B]
+    return kw, P
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_batches(case):
+    rng = np.random.default_rng(800_000 + case)
+    kw, P = _random_batch_case(rng)
+    name = (f"random batch {case}: D={kw['head_dim']} {kw['kv_dtype']} "
+            f"G={kw['num_q_heads'] // kw['num_kv_heads']} B={len(kw['q_lens'])}")
+    wl = edge(name, seed=800_000 + case, **kw)
+    got, ref, info = check(wl, name, partition_tokens=P)
+    dev = wl.to("cuda:0")
+    plan = pav.plan_for(dev, device=0, partition_tokens=P)
+    dt = torch.float32 if wl.out_dtype == "fp32" else torch.bfloat16
+    out = torch.full((wl.total_q, wl.num_q_heads, wl.head_dim), float("nan"), dtype=dt,
+                     device="cuda:0")
+    pav.pa_decode_verify_fused(plan, None, dev.q, dev.k_pool, dev.v_pool, dev.block_table,
+                               dev.k_scales, dev.v_scales, dev.sinks, out)
+    torch.cuda.synchronize()
+    pav.pa_free(plan)
+    compare(f"{name}, single launch ({info['work_items']} items)", out.float().cpu().numpy(),
+            ref, out_bf16=(wl.out_dtype == "bf16"))
+
+
 # FP8 V with its scales multiplied by f: the output scales by f, so the
 # gate applies to gpu / f against oracle / f (fp32 output: the division is
 # the only rounding added). p w enters an fp16 product; scales far below 1
