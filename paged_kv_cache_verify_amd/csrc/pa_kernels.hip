@@ -1,14 +1,15 @@
 // gfx950 kernels for paged verify attention.
 //
-// Partition kernel: one workgroup per work item (and per CU) = the keys
-// [key_begin, key_end) of one (sequence, KV head), all the item's packed
-// rows of that KV head. The waves form NG token groups (2 to 4, by layout):
-// group g takes the item's 32-token chunks (two 16-token pages) g, g + NG,
-// ..., each through an LDS ring of its own that the group's loader wave
-// fills by direct global-to-LDS loads (K as token rows with a 16-byte chunk
-// swizzle, V into an XOR-swizzled token-major tile); one workgroup barrier
-// per step recycles a stage in every ring. Within a group, compute wave r owns
-// row tile r (16 rows) and, per chunk,
+// Partition kernel: one workgroup per work item (one or two per CU, by
+// layout; the single-launch call runs a persistent grid that takes the items
+// in turn) = the keys [key_begin, key_end) of one (sequence, KV head), the
+// item's packed rows of that KV head. The waves form NG token groups (1 to
+// 4, by layout): group g takes the item's 32-token chunks (two 16-token
+// pages) g, g + NG, ..., each through an LDS ring of its own that the group's
+// loader wave fills by direct global-to-LDS loads (K as token rows with a
+// 16-byte chunk swizzle, V into an XOR-swizzled token-major tile); one
+// workgroup barrier per step recycles a stage in every ring. Within a group,
+// compute wave r owns row tile r (16 rows) and, per chunk,
 //   1. computes S^T = K Q^T, tokens on the M index: bf16 K with
 //      v_mfma_f32_16x16x32_bf16; FP8 K codes as stored with the e4m3 MFMA
 //      (v_mfma_f32_16x16x128_f8f6f4) against the query split once into two
@@ -588,8 +589,8 @@ __device__ __forceinline__ f32x4 pv_tile(bf16x8 v, bf16x8 p_hi, bf16x8 p_lo, f32
   return mfma_bf16(v, p_lo, o);
 }
 
-// One chunk for the wave's 16-row tile, bf16 KV: kv is the ring stage (K of
-// the two pages in operand order, then the V tile).
+// One chunk for the wave's 16-row tile, bf16 KV: kv is the ring stage (the
+// K tiles of the two pages as swizzled token rows, then the V tile).
 template <int D>
 __device__ __forceinline__ void compute_chunk(WaveState<D, false>& S, const unsigned char* kv,
                                               int tok0, int tv0, int tv1, int L, int q, int W,
